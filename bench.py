@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Time the GDN decode block on one MI355X.
+
+A step is one decode launch of the whole block over one batch of rows. The
+timed launches are captured in HIP graphs that rotate over `layers` copies of
+the weights, each copy with its own conv and SSM state pools, so the 256 MB
+MALL cannot keep a layer resident between its launches (the method of "vLLM PR
+#60833", Validation / Per launch: graphs of 46 launches, weights rotated past
+the MALL). Time comes from HIP events on the stream the block is launched on.
+
+Prints one JSON line: µs per launch at the headline row count, the roofline
+(algorithmic HBM bytes per launch / launch time against 8 TB/s), a sweep over
+row counts, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN block µs/launch at 1-16 rows; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_deltanet_linear_decode_amd", "csrc", "gdn_block.hip")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Rotation:
+    """`layers` copies of one layer's weights and state pools on the device."""
+
+    def __init__(self, shape, layers, max_rows, seed=0):
+        import torch
+
+        from gated_deltanet_linear_decode_amd import synth
+        from gated_deltanet_linear_decode_amd.block import GdnBlock
+
+        dev = torch.device("cuda:0")
+        self.shape, self.dev = shape, dev
+        self.blk = GdnBlock(shape, max_rows=max_rows, device=dev)
+        self.w_cpu = synth.make_weights(shape, seed)
+        self.call_cpu = synth.make_call(shape, max_rows, seed, pads=False)
+        self.copies = []
+        for i in range(layers):
+            w = synth.GdnWeights(**{k: (v.to(dev).clone() if v is not None else None)
+                                    for k, v in self.w_cpu.__dict__.items()})
+            c = dict(
+                w=w, ws=self.blk.weights_struct(w),
+                x=self.call_cpu.x.to(dev).clone(), res=self.call_cpu.residual.to(dev).clone(),
+                conv=self.call_cpu.conv_state.to(dev).clone(), ssm=self.call_cpu.ssm_state.to(dev).clone(),
+                idx=self.call_cpu.state_idx.to(dev).clone(),
+                core=torch.empty(max_rows, shape.value_dim, dtype=torch.bfloat16, device=dev))
+            self.copies.append(c)
+        torch.cuda.synchronize()
+
+    def launch(self, i, rows):
+        c = self.copies[i % len(self.copies)]
+        self.blk.decode(c["x"][:rows], c["res"][:rows], None, c["conv"], c["ssm"], c["idx"][:rows],
+                        c["core"][:rows], weights_struct=c["ws"])
+
+    def graph(self, n, rows, start=0):
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(len(self.copies)):
+                self.launch(i, rows)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                self.launch(start + i, rows)
+        return g
+
+    def time(self, rows, steps, warmup):
+        """Average µs per launch over exactly `steps` launches (after `warmup`)."""
+        import torch
+        per = 4 * len(self.copies)           # launches per graph: whole rotations, >= 46 at 12 copies
+        while per < 46:
+            per += len(self.copies)
+        g = self.graph(per, rows)
+        rem = steps % per
+        g_rem = self.graph(rem, rows) if rem else None
+        for _ in range(max(1, warmup // per)):
+            g.replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps // per):
+            g.replay()
+        if g_rem is not None:
+            g_rem.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) * 1000.0 / steps
+
+
+def cpu_baseline(shape, rot, rows, seconds):
+    """The oracle on the same workload (same bytes), timed for about `seconds`."""
+    import numpy as np
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16).copy()  # noqa: E731
+    cfg = dict(hidden=shape.hidden, num_k_heads=shape.num_k_heads, head_k_dim=shape.head_k_dim,
+               num_v_heads=shape.num_v_heads, head_v_dim=shape.head_v_dim, conv_width=shape.conv_width,
+               ssm_state_dtype=shape.ssm_state_dtype, has_residual=shape.has_residual,
+               qkvz_format=shape.qkvz_format, norm_eps=shape.norm_eps,
+               gated_norm_eps=shape.gated_norm_eps, l2norm_eps=shape.l2norm_eps)
+    w = {k: (bits(v) if v.dtype == torch.bfloat16 else v.numpy()) for k, v in rot.w_cpu.tensors().items()}
+    c = rot.call_cpu
+    x, res = bits(c.x[:rows]), bits(c.residual[:rows])
+    conv = bits(c.conv_state)
+    ssm = bits(c.ssm_state) if c.ssm_state.dtype == torch.bfloat16 else c.ssm_state.numpy()
+    idx = c.state_idx[:rows].numpy()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_block(cfg, w, x, res, conv, ssm, idx)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=el / n * 1e6, unit="µs/launch", cores=threads, kind="oracle",
+                sample=f"{n} oracle decode calls of the {rows}-row step of {shape.name} "
+                       f"(float64 numpy, {threads} BLAS threads), {el:.1f} s")
+
+
+def main():
+    from gated_deltanet_linear_decode_amd import configs
+
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4800)
+    ap.add_argument("--warmup", type=int, default=480)
+    ap.add_argument("--config", default=configs.TP8_RANK_BF16.name, choices=sorted(configs.ALL))
+    ap.add_argument("--rows", type=int, default=8)
+    ap.add_argument("--sweep-rows", default="1,2,4,8,12,16")
+    ap.add_argument("--sweep-steps", type=int, default=960)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the block shards by heads with no exchange inside it; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    shape = configs.ALL[args.config]
+    sweep_rows = [int(r) for r in args.sweep_rows.split(",") if r]
+    max_rows = max([args.rows] + sweep_rows)
+    assert max_rows <= 16
+    log(f"setting up {shape.layers} layer copies of {shape.name} (max_rows {max_rows})")
+    rot = Rotation(shape, shape.layers, max_rows)
+    log(f"timing {args.steps} launches at {args.rows} rows")
+    torch.cuda.synchronize()
+    us = rot.time(args.rows, args.steps, args.warmup)
+    algo = configs.algorithmic_bytes(shape, args.rows)
+    gbs = algo / (us * 1e-6) / 1e9
+    sweep = {}
+    for r in sweep_rows:
+        t = rot.time(r, args.sweep_steps, args.sweep_steps // 4)
+        b = configs.algorithmic_bytes(shape, r)
+        sweep[str(r)] = dict(us=round(t, 3), algo_bytes=b, gbs=round(b / (t * 1e-6) / 1e9, 1),
+                             frac=round(b / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+        log(f"rows {r}: {t:.2f} us/launch")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        entry = tr.get(shape.name, {}).get(str(args.rows))
+        if tr.get("kernel_source_hash") == kernel_source_hash() and entry:
+            traffic = entry["bytes_per_launch"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(shape, rot, args.rows, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(us, 3),
+        "unit": "µs/launch",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": shape.name, "rows": args.rows, "hidden": shape.hidden,
+            "key_heads": f"{shape.num_k_heads}x{shape.head_k_dim}",
+            "value_heads": f"{shape.num_v_heads}x{shape.head_v_dim}",
+            "ssm_state": shape.ssm_state_dtype, "in_proj_qkvz": shape.qkvz_format,
+            "has_residual": shape.has_residual, "layers_rotated": shape.layers,
+            "state_slots": shape.num_state_slots,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algo_bytes_per_launch": algo, "kernel": "gdn_block decode (norm + gemv + gdn launches)",
+        },
+        "sweep": sweep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

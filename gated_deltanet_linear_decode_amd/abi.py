@@ -1,0 +1,95 @@
+"""ctypes binding of the C ABI in include/gdn_block.h, function for function.
+
+Argument marshalling only: every step of the block runs in the HIP library.
+Loading fails loudly when the library is not built; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_void_p
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn_block.so")
+
+GDN_OK = 0
+GDN_E_INVALID_ARG = -1
+GDN_E_UNSUPPORTED = -2
+GDN_E_HIP = -3
+GDN_FMT_BF16 = 0
+GDN_FMT_MXFP4 = 1
+GDN_STATE_F32 = 0
+GDN_STATE_BF16 = 1
+GDN_MAX_ROWS = 16
+
+EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error")
+
+
+class GdnBlockConfig(ctypes.Structure):
+    _fields_ = [
+        ("hidden", c_int32), ("num_k_heads", c_int32), ("head_k_dim", c_int32),
+        ("num_v_heads", c_int32), ("head_v_dim", c_int32), ("conv_width", c_int32),
+        ("num_state_slots", c_int32), ("max_rows", c_int32), ("qkvz_format", c_int32),
+        ("ssm_state_dtype", c_int32), ("has_residual", c_int32),
+        ("norm_eps", c_float), ("gated_norm_eps", c_float), ("l2norm_eps", c_float),
+    ]
+
+
+class GdnBlockWeights(ctypes.Structure):
+    _fields_ = [
+        ("norm_w", c_void_p), ("w_qkvz", c_void_p), ("w_qkvz_scales", c_void_p), ("w_ba", c_void_p),
+        ("conv_w", c_void_p), ("A_log", c_void_p), ("dt_bias", c_void_p), ("gated_norm_w", c_void_p),
+    ]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgdn_block.so (built in-tree by gated_deltanet_linear_decode_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m gated_deltanet_linear_decode_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.gdn_block_create.argtypes = [POINTER(GdnBlockConfig), POINTER(c_void_p)]
+        lib.gdn_block_create.restype = c_int
+        lib.gdn_block_decode.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(GdnBlockWeights), c_void_p,
+                                         c_void_p, c_void_p, c_int32, c_void_p, c_void_p]
+        lib.gdn_block_decode.restype = c_int
+        lib.gdn_block_destroy.argtypes = [c_void_p]
+        lib.gdn_block_destroy.restype = None
+        lib.gdn_block_last_error.argtypes = [c_void_p]
+        lib.gdn_block_last_error.restype = c_char_p
+        _lib = lib
+    return _lib
+
+
+def gdn_block_last_error(handle) -> str:
+    return load().gdn_block_last_error(handle).decode()
+
+
+def gdn_block_create(cfg: GdnBlockConfig) -> c_void_p:
+    h = c_void_p()
+    rc = load().gdn_block_create(ctypes.byref(cfg), ctypes.byref(h))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(None))
+    return h
+
+
+def gdn_block_decode(handle, x: int, residual: int, weights: GdnBlockWeights, conv_state: int,
+                     ssm_state: int, state_idx: int, rows: int, core_out: int, stream: int) -> None:
+    rc = load().gdn_block_decode(handle, x, residual, ctypes.byref(weights), conv_state, ssm_state,
+                                 state_idx, rows, core_out, stream)
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(handle))
+
+
+def gdn_block_destroy(handle) -> None:
+    if handle:
+        load().gdn_block_destroy(handle)

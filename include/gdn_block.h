@@ -1,0 +1,138 @@
+/*
+ * gdn_block.h -- C ABI of the Gated DeltaNet (GDN) decode block for MI355X (gfx950).
+ *
+ * One gdn_block_decode() call runs a GDN layer's decode front for 1..16 rows,
+ * the launch called "K1" on "sgl-amd-mono PR #89" (Modifications) and the "GDN
+ * block" on "vLLM PR #60833" (Details / Launches):
+ *
+ *   1. residual add + Gemma RMSNorm: h = bf16(x + residual), residual <- h,
+ *      xn = bf16(h * (mean(h^2) + eps)^-1/2 * (1 + norm_w));
+ *   2. in_proj_qkvz and in_proj_ba: y = bf16(W xn), bf16 weights, or MXFP4
+ *      in_proj_qkvz with xn quantised to MXFP4 per 32-element block
+ *      ("vLLM PR #60833", Details / MoE and MXFP4 layouts);
+ *   3. causal depthwise conv update (width 4, no bias) + SiLU over the q|k|v
+ *      channels, conv state rolled in place;
+ *   4. g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b); q, k
+ *      L2-normalised, q scaled by dk^-1/2;
+ *   5. gated delta rule on the cached state S (dk x dv per value head):
+ *      S <- exp(g) S; S <- S + k (beta (v - S^T k))^T; o = S^T q, computed in
+ *      f32 and stored back f32 or RNE bf16 ("sgl-amd-mono PR #89", Kernel checks);
+ *   6. RMSNormGated over each head, norm before gate:
+ *      core = bf16(bf16(o) * rstd * gated_norm_w * SiLU(z)).
+ *
+ * A row whose state index is <= 0 is a pad row: its core row is written as
+ * +0.0, and neither conv nor SSM state is touched; its residual row is still
+ * written ("sgl-amd-mono PR #89", Modifications; "SGLang PR #43558", Accuracy:
+ * pad rows at slot -1).
+ *
+ * Layouts (all row-major, caller-owned device memory):
+ *   x, residual       [rows, H] bf16
+ *   norm_w            [H] bf16 (Gemma form: the scale is 1 + norm_w)
+ *   w_qkvz (BF16)     [Nqkvz, H] bf16, Nqkvz = 2*nk*dk + 2*nv*dv, K contiguous
+ *   w_qkvz (MXFP4)    [Nqkvz, H/2] uint8 e2m1 codes, low nibble = even k,
+ *   w_qkvz_scales     [Nqkvz, H/32] uint8 e8m0 (2^(byte-127)), MXFP4 only
+ *                     Output columns are grouped per key head g:
+ *                     [q_g (dk) | k_g (dk) | v_g (r*dv) | z_g (r*dv)], r = nv/nk.
+ *   w_ba              [2*nv, H] bf16, grouped per key head: [b_g (r) | a_g (r)]
+ *   conv_w            [Cd, W] bf16, Cd = 2*nk*dk + nv*dv channels ordered
+ *                     q (nk*dk) | k (nk*dk) | v (nv*dv); tap W-1 multiplies
+ *                     the newest input
+ *   A_log             [nv] f32;  dt_bias [nv] bf16;  gated_norm_w [dv] bf16
+ *   conv_state        [num_state_slots, W-1, Cd] bf16: the W-1 previous raw
+ *                     q|k|v projection outputs, oldest first
+ *   ssm_state         [num_state_slots, nv, dk, dv] f32 or bf16
+ *   state_idx         [rows] int32 in device memory; value head h uses key head h / r
+ *   core_out          [rows, nv*dv] bf16
+ *
+ * Errors: every function returns GDN_OK (0) or a negative code; the message
+ * is kept per handle (gdn_block_last_error). A failed check enqueues nothing.
+ */
+#ifndef GDN_BLOCK_H
+#define GDN_BLOCK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_OK 0
+#define GDN_E_INVALID_ARG (-1) /* a null or misaligned pointer, a bad row count or config value */
+#define GDN_E_UNSUPPORTED (-2) /* a configuration this library refuses (every reason listed) */
+#define GDN_E_HIP (-3)         /* a HIP runtime call failed (message holds hipGetErrorString) */
+
+#define GDN_FMT_BF16 0   /* in_proj_qkvz stored as bf16 */
+#define GDN_FMT_MXFP4 1  /* in_proj_qkvz stored as OCP MXFP4: e2m1 codes + e8m0 per 32 K */
+
+#define GDN_STATE_F32 0
+#define GDN_STATE_BF16 1
+
+#define GDN_MAX_ROWS 16
+
+typedef struct gdn_block_config {
+  int32_t hidden;          /* H; a multiple of 256 */
+  int32_t num_k_heads;     /* nk */
+  int32_t head_k_dim;      /* dk: 32, 64 or 128 */
+  int32_t num_v_heads;     /* nv; a multiple of nk */
+  int32_t head_v_dim;      /* dv: equal to dk */
+  int32_t conv_width;      /* W; must be 4 */
+  int32_t num_state_slots; /* slots in the conv and SSM state pools */
+  int32_t max_rows;        /* largest row count a decode call may pass, 1..16 */
+  int32_t qkvz_format;     /* GDN_FMT_BF16 or GDN_FMT_MXFP4 */
+  int32_t ssm_state_dtype; /* GDN_STATE_F32 or GDN_STATE_BF16 */
+  int32_t has_residual;    /* 0: the layer with no residual input (residual is written = x) */
+  float norm_eps;          /* Gemma RMSNorm eps (1e-6) */
+  float gated_norm_eps;    /* RMSNormGated eps (1e-6) */
+  float l2norm_eps;        /* eps inside the q/k L2 norm's square root (1e-6) */
+} gdn_block_config;
+
+typedef struct gdn_block_weights {
+  const void* norm_w;        /* [H] bf16 */
+  const void* w_qkvz;        /* [Nqkvz, H] bf16 or [Nqkvz, H/2] e2m1 bytes */
+  const void* w_qkvz_scales; /* [Nqkvz, H/32] e8m0 bytes (MXFP4 only, else ignored) */
+  const void* w_ba;          /* [2*nv, H] bf16 */
+  const void* conv_w;        /* [Cd, W] bf16 */
+  const float* A_log;        /* [nv] f32 */
+  const void* dt_bias;       /* [nv] bf16 */
+  const void* gated_norm_w;  /* [dv] bf16 */
+} gdn_block_weights;
+
+typedef struct gdn_block* gdn_block_t;
+
+/* Validate cfg and build a handle. Every unsupported setting is refused with
+ * GDN_E_UNSUPPORTED and all reasons listed in the message (the startup
+ * refusals of "sgl-amd-mono PR #89", Modifications / Refusals; "vLLM PR
+ * #60833", Details / Refusals). Validation touches no device; on success the
+ * handle owns device scratch sized for cfg->max_rows, allocated on the current
+ * HIP device. On failure *out is NULL and gdn_block_last_error(NULL) holds
+ * the message (per thread). */
+int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out);
+
+/* Enqueue one decode step of `rows` rows on `stream` (a hipStream_t; NULL is
+ * the default stream). Asynchronous: no host sync, no allocation, so it can
+ * be captured into a HIP graph. All pointers are device pointers aligned to
+ * 16 bytes. x is read; residual is read (when the layer has one) and written
+ * with h; conv_state and ssm_state are updated in place at the slots named by
+ * the valid rows; core_out is written. rows == 0 enqueues nothing and
+ * returns GDN_OK; rows < 0 or rows > max_rows is GDN_E_INVALID_ARG.
+ * Precondition: the valid state indices of one call are distinct. An index
+ * >= num_state_slots is handled like a pad row (zero core, no state access),
+ * so no index can make the kernels touch memory outside the pools. The handle's scratch is
+ * shared by its calls: calls on one handle must be ordered (one stream). */
+int gdn_block_decode(gdn_block_t blk, const void* x, void* residual, const gdn_block_weights* w,
+                     void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
+                     void* core_out, void* stream);
+
+/* Free the handle and its scratch (NULL is a no-op). Waits for nothing: the
+ * caller must make sure no enqueued decode still uses it. */
+void gdn_block_destroy(gdn_block_t blk);
+
+/* The last error message of a handle, or of this thread's last failed
+ * gdn_block_create when blk is NULL. Never NULL; "" when there was none. */
+const char* gdn_block_last_error(gdn_block_t blk);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_BLOCK_H */

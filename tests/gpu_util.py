@@ -1,0 +1,96 @@
+"""Shared pieces of the GPU tests: moving a synthetic call to the device,
+running the HIP block through the C ABI, and the parity rule.
+
+Parity rule for floating-point outputs (bf16 core, conv state, SSM state):
+|gpu - oracle| <= max(2e-2, one bf16 ulp of the oracle value) element by
+element, and cosine >= 0.9999 over the written elements. The residual, pad
+rows and untouched slots are compared bit for bit.
+"""
+import sys
+
+import numpy as np
+import torch
+
+from gated_deltanet_linear_decode_amd.block import GdnBlock
+from gated_deltanet_linear_decode_amd.synth import GdnCall, GdnWeights
+from oracle import gdn as og
+from tests.helpers import oracle_state, run_oracle, u16
+
+ABS_TOL = 2e-2
+COS_MIN = 0.9999
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def weights_to(w: GdnWeights, dev) -> GdnWeights:
+    return GdnWeights(**{k: (v.to(dev) if v is not None else None) for k, v in w.__dict__.items()})
+
+
+def call_to(c: GdnCall, dev) -> GdnCall:
+    return GdnCall(**{k: v.to(dev).contiguous() for k, v in c.__dict__.items()})
+
+
+def run_gpu(blk: GdnBlock, shape, wd: GdnWeights, cd: GdnCall, rows=None):
+    """Run one decode on copies of the device inputs; returns CPU tensors."""
+    R = cd.x.shape[0] if rows is None else rows
+    res = cd.residual.clone()
+    conv = cd.conv_state.clone()
+    ssm = cd.ssm_state.clone()
+    core = torch.full((R, shape.value_dim), float("nan"), dtype=torch.bfloat16, device=cd.x.device)
+    blk.decode(cd.x, res, wd, conv, ssm, cd.state_idx, core)
+    torch.cuda.synchronize()
+    return dict(core=core.cpu(), residual=res.cpu(), conv_state=conv.cpu(), ssm_state=ssm.cpu())
+
+
+def _ulp_bf16(r):
+    a = np.maximum(np.abs(r), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def close(name, got, ref, bf16=True):
+    """Assert the parity rule; returns (max_abs, count above ABS_TOL)."""
+    g = og.bf16_to_f64(got) if bf16 else np.asarray(got, np.float64)
+    r = og.bf16_to_f64(ref) if bf16 else np.asarray(ref, np.float64)
+    g, r = g.reshape(-1), r.reshape(-1)
+    if g.size == 0:
+        return 0.0, 0
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    err = np.abs(g - r)
+    bound = np.maximum(ABS_TOL, _ulp_bf16(r)) if bf16 else np.full_like(r, ABS_TOL)
+    bad = err > bound
+    assert not bad.any(), (f"{name}: {bad.sum()} of {err.size} outside the bound; worst err "
+                           f"{err.max():.4g} at {np.argmax(err)} (gpu {g[np.argmax(err)]}, oracle {r[np.argmax(err)]})")
+    nr, ng = np.linalg.norm(r), np.linalg.norm(g)
+    if nr > 0:
+        cos = float(g @ r / (nr * ng))
+        assert cos >= COS_MIN, f"{name}: cosine {cos}"
+    return float(err.max()), int((err > ABS_TOL).sum())
+
+
+def check_parity(shape, w, call, out, label=""):
+    """Compare one GPU decode's outputs with the oracle's."""
+    ref = run_oracle(shape, w, call)
+    idx = call.state_idx.numpy()
+    valid = idx > 0
+    core = u16(out["core"])
+    # residual: bit for bit
+    assert np.array_equal(u16(out["residual"]), ref["residual"]), f"{label}: residual differs"
+    # pad rows: all +0.0
+    assert np.all(core[~valid] == 0), f"{label}: pad row core not +0"
+    stats = {}
+    stats["core"] = close(f"{label} core", core[valid], ref["core"][valid])
+    slots = idx[valid]
+    conv_g, conv_r = u16(out["conv_state"]), ref["conv_state"]
+    bf16_state = shape.ssm_state_dtype == "bf16"
+    ssm_g, ssm_r = oracle_state(out["ssm_state"]), ref["ssm_state"]
+    untouched = np.setdiff1d(np.arange(shape.num_state_slots), slots)
+    assert np.array_equal(conv_g[untouched], u16(call.conv_state)[untouched]), f"{label}: untouched conv slot changed"
+    assert np.array_equal(ssm_g[untouched], oracle_state(call.ssm_state)[untouched]), \
+        f"{label}: untouched ssm slot changed"
+    if len(slots):
+        stats["conv"] = close(f"{label} conv_state", conv_g[slots], conv_r[slots])
+        stats["ssm"] = close(f"{label} ssm_state", ssm_g[slots], ssm_r[slots], bf16=bf16_state)
+    return stats

@@ -1,0 +1,84 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/gdn_block.h declares, its structs match the header, and create()
+refuses bad configurations (listing every reason) without touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_linear_decode_amd import abi, configs
+from gated_deltanet_linear_decode_amd.block import make_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn_block.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_block_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = abi.load()
+    declared = _declared_functions()
+    assert declared == sorted(abi.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct gdn_block_config \{(.*?)\} gdn_block_config;", src, re.S).group(1)
+    fields = re.findall(r"(int32_t|float)\s+([\w ,]+);", re.sub(r"/\*.*?\*/", "", body, flags=re.S))
+    names = [n.strip() for _, group in fields for n in group.split(",")]
+    assert names == [f[0] for f in abi.GdnBlockConfig._fields_]
+    assert ctypes.sizeof(abi.GdnBlockConfig) == 4 * len(names)
+    wbody = re.search(r"typedef struct gdn_block_weights \{(.*?)\} gdn_block_weights;", src, re.S).group(1)
+    wnames = re.findall(r"\*\s*(\w+);", wbody)
+    assert wnames == [f[0] for f in abi.GdnBlockWeights._fields_]
+
+
+def _cfg(**kw):
+    c = make_config(configs.TINY)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,needle", [
+    ("hidden", 100, "hidden"),
+    ("num_v_heads", 3, "num_v_heads"),
+    ("head_k_dim", 48, "head_k_dim"),
+    ("head_v_dim", 64, "head_v_dim"),
+    ("conv_width", 3, "conv_width"),
+    ("num_state_slots", 1, "num_state_slots"),
+    ("max_rows", 17, "max_rows"),
+    ("max_rows", 0, "max_rows"),
+    ("qkvz_format", 9, "qkvz_format"),
+    ("ssm_state_dtype", 2, "ssm_state_dtype"),
+    ("has_residual", 2, "has_residual"),
+    ("norm_eps", 0.0, "eps"),
+])
+def test_create_refuses_each_bad_field(field, value, needle):
+    with pytest.raises(abi.GdnError) as e:
+        abi.gdn_block_create(_cfg(**{field: value}))
+    assert e.value.code == abi.GDN_E_UNSUPPORTED
+    assert needle in str(e.value)
+
+
+def test_create_lists_every_reason():
+    with pytest.raises(abi.GdnError) as e:
+        abi.gdn_block_create(_cfg(hidden=100, conv_width=5, max_rows=40, has_residual=3))
+    msg = str(e.value)
+    for needle in ("hidden", "conv_width", "max_rows", "has_residual"):
+        assert needle in msg
+
+
+def test_null_arguments_are_rejected_on_the_host():
+    lib = abi.load()
+    assert lib.gdn_block_create(None, None) == abi.GDN_E_INVALID_ARG
+    assert "NULL" in abi.gdn_block_last_error(None)
+    assert lib.gdn_block_decode(None, None, None, None, None, None, None, 1, None, None) == abi.GDN_E_INVALID_ARG
+    lib.gdn_block_destroy(None)  # a no-op

@@ -1,0 +1,76 @@
+"""GPU parity: the HIP block against the CPU oracle, element by element, on the
+same seeded inputs, at the tiny shape (many seeds, ragged row counts) and at
+the full sizes of each workload (all rows, pad rows, all-pad calls)."""
+import pytest
+import torch
+
+from gated_deltanet_linear_decode_amd import configs, synth
+from gated_deltanet_linear_decode_amd.block import GdnBlock
+from tests.gpu_util import call_to, check_parity, note, run_gpu, weights_to
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _case(shape, rows, seed, *, pads=None, all_pad=False, stress=False, max_rows=None):
+    note(f"case {shape.name} rows={rows} seed={seed} pads={pads} all_pad={all_pad} stress={stress}")
+    w = synth.make_weights(shape, seed, gated_norm_stress=stress)
+    call = synth.make_call(shape, rows, seed, pads=pads, all_pad=all_pad)
+    blk = GdnBlock(shape, max_rows=max_rows or max(rows, shape.max_rows), device=DEV)
+    out = run_gpu(blk, shape, weights_to(w, DEV), call_to(call, DEV))
+    blk.close()
+    stats = check_parity(shape, w, call, out, label=f"{shape.name}/r{rows}/s{seed}")
+    note(f"  ok {stats}")
+    return stats
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("state", ["f32", "bf16"])
+def test_tiny_one_row(seed, state):
+    _case(configs.TINY.with_(ssm_state_dtype=state), 1, seed)
+
+
+@pytest.mark.parametrize("rows", [1, 2, 3, 7, 13, 16])
+@pytest.mark.parametrize("has_res", [True, False])
+def test_tiny_ragged_rows_with_pads(rows, has_res):
+    shape = configs.TINY.with_(num_state_slots=24, pad_rows=True, has_residual=has_res, rows=(16,))
+    _case(shape, rows, 100 + rows)
+
+
+@pytest.mark.parametrize("dk", [32, 64, 128])
+def test_head_dims(dk):
+    shape = configs.GdnShape("heads", hidden=512, num_k_heads=2, head_k_dim=dk, num_v_heads=6,
+                             head_v_dim=dk, num_state_slots=12, pad_rows=True, rows=(8,))
+    _case(shape, 8, 7)
+
+
+def test_largest_hidden():
+    shape = configs.GdnShape("wide", hidden=16384, num_k_heads=1, head_k_dim=64, num_v_heads=2,
+                             head_v_dim=64, num_state_slots=20, rows=(16,), pad_rows=True)
+    _case(shape, 16, 3)
+
+
+@pytest.mark.parametrize("rows", configs.TP8_RANK_BF16.rows)
+def test_tp8_rank_bf16_state_layer0(rows):
+    _case(configs.TP8_RANK_BF16, rows, 11)
+
+
+@pytest.mark.parametrize("rows", configs.TP8_RANK_F32.rows)
+def test_tp8_rank_f32_state_pads(rows):
+    _case(configs.TP8_RANK_F32, rows, 12)
+
+
+def test_tp8_rank_all_pad():
+    _case(configs.TP8_RANK_F32, 1, 13, all_pad=True)
+    _case(configs.TP8_RANK_F32, 4, 14, all_pad=True)
+
+
+@pytest.mark.parametrize("rows", [1, 4, 8])
+def test_dense_full_width(rows):
+    _case(configs.DENSE_FULL, rows, 15)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tp8_rank_bf16_state_layer0", "dense_full_width"])
+def test_gated_norm_weight_near_one(name):
+    shape = configs.ALL[name]
+    _case(shape, min(4, shape.max_rows), 16, stress=True, pads=False)

@@ -1,0 +1,169 @@
+"""GPU-against-GPU properties that hold exactly ("sgl-amd-mono PR #89", Kernel
+checks): batch invariance, the bf16 state being the f32 state rounded, graph
+replay equal to eager, run-to-run determinism; plus the decode call's host-side
+argument checks with a live handle."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_decode_amd import abi, configs, synth
+from gated_deltanet_linear_decode_amd.block import GdnBlock
+from tests.gpu_util import call_to, note, run_gpu, weights_to
+from tests.helpers import u16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _bits(t):
+    return u16(t) if t.dtype == torch.bfloat16 else t.numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tp8_rank_f32_state_pads"])
+def test_batch_invariance(name):
+    """A probe row's outputs do not change with the other rows or the width."""
+    shape = configs.ALL[name].with_(num_state_slots=40, rows=(16,), pad_rows=False)
+    w = weights_to(synth.make_weights(shape, 21), DEV)
+    blk = GdnBlock(shape, max_rows=16, device=DEV)
+    base = synth.make_call(shape, 16, 21)
+    probe_slot = int(base.state_idx[0])
+    ref = None
+    for width in (1, 2, 5, 8, 9, 16):
+        for pos in sorted({0, width - 1, width // 2}):
+            note(f"batch invariance {name} width={width} pos={pos}")
+            other = synth.make_call(shape, width, 1000 + width * 17 + pos)
+            idx = other.state_idx.clone()
+            idx[idx == probe_slot] = int(base.state_idx[1])   # keep slots distinct
+            idx[pos] = probe_slot
+            x, res = other.x.clone(), other.residual.clone()
+            x[pos], res[pos] = base.x[0], base.residual[0]
+            call = synth.GdnCall(x, res, base.conv_state, base.ssm_state, idx)
+            out = run_gpu(blk, shape, w, call_to(call, DEV))
+            got = (u16(out["core"][pos]), u16(out["residual"][pos]), u16(out["conv_state"][probe_slot]),
+                   _bits(out["ssm_state"][probe_slot]))
+            if ref is None:
+                ref = got
+            for a, b in zip(ref, got):
+                assert np.array_equal(a, b), f"width {width} pos {pos}"
+    blk.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "tp8_rank_bf16_state_layer0"])
+def test_bf16_state_is_f32_state_rounded(name):
+    shape_b = configs.ALL[name].with_(ssm_state_dtype="bf16", pad_rows=True, rows=(8,), num_state_slots=16)
+    shape_f = shape_b.with_(ssm_state_dtype="f32")
+    rows = min(8, shape_b.num_state_slots - 1)
+    w = weights_to(synth.make_weights(shape_b, 22), DEV)
+    call_b = synth.make_call(shape_b, rows, 22)
+    call_f = synth.GdnCall(call_b.x, call_b.residual, call_b.conv_state, call_b.ssm_state.float(),
+                           call_b.state_idx)
+    bb = GdnBlock(shape_b, max_rows=8, device=DEV)
+    bf = GdnBlock(shape_f, max_rows=8, device=DEV)
+    out_b = run_gpu(bb, shape_b, w, call_to(call_b, DEV))
+    out_f = run_gpu(bf, shape_f, w, call_to(call_f, DEV))
+    assert np.array_equal(u16(out_b["core"]), u16(out_f["core"]))
+    assert np.array_equal(u16(out_b["conv_state"]), u16(out_f["conv_state"]))
+    assert np.array_equal(u16(out_b["ssm_state"]), u16(out_f["ssm_state"].to(torch.bfloat16)))
+    bb.close()
+    bf.close()
+
+
+def test_determinism():
+    shape = configs.TP8_RANK_F32
+    w = weights_to(synth.make_weights(shape, 23), DEV)
+    cd = call_to(synth.make_call(shape, 16, 23), DEV)
+    blk = GdnBlock(shape, device=DEV)
+    a = run_gpu(blk, shape, w, cd)
+    b = run_gpu(blk, shape, w, cd)
+    for k in a:
+        assert torch.equal(a[k].view(torch.int16) if a[k].dtype == torch.bfloat16 else a[k],
+                           b[k].view(torch.int16) if b[k].dtype == torch.bfloat16 else b[k]), k
+    blk.close()
+
+
+def test_graph_replay_equals_eager():
+    """Widths 8, 1, 3, 8, 2, 5 in one graph on one state pool, replayed 200 times."""
+    shape = configs.TP8_RANK_BF16.with_(num_state_slots=32, rows=(8,), has_residual=True, pad_rows=True)
+    w = weights_to(synth.make_weights(shape, 24), DEV)
+    blk = GdnBlock(shape, max_rows=8, device=DEV)
+    ws = blk.weights_struct(w)
+    widths = (8, 1, 3, 8, 2, 5)
+    calls = [call_to(synth.make_call(shape, r, 300 + i), DEV) for i, r in enumerate(widths)]
+    conv0, ssm0 = calls[0].conv_state.clone(), calls[0].ssm_state.clone()
+    conv, ssm = conv0.clone(), ssm0.clone()
+    res = [c.residual.clone() for c in calls]
+    cores = [torch.zeros(r, shape.value_dim, dtype=torch.bfloat16, device=DEV) for r in widths]
+
+    def step_all():
+        for i, c in enumerate(calls):
+            blk.decode(c.x, res[i], None, conv, ssm, c.state_idx, cores[i], weights_struct=ws)
+
+    def reset():
+        conv.copy_(conv0)
+        ssm.copy_(ssm0)
+        for i, c in enumerate(calls):
+            res[i].copy_(c.residual)
+
+    reset()
+    step_all()
+    torch.cuda.synchronize()
+    eager = [conv.clone(), ssm.clone()] + [r.clone() for r in res] + [c.clone() for c in cores]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        reset()
+        step_all()            # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_all()
+    mismatches = 0
+    for rep in range(200):
+        reset()
+        for c in cores:
+            c.fill_(1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        got = [conv, ssm] + res + cores
+        for a, b in zip(eager, got):
+            if not torch.equal(a.view(torch.int16), b.view(torch.int16)):
+                mismatches += 1
+        if rep % 50 == 0:
+            note(f"graph replay {rep}: mismatches so far {mismatches}")
+    assert mismatches == 0
+    blk.close()
+
+
+def test_decode_rejects_bad_arguments_on_the_host():
+    shape = configs.TINY
+    w = weights_to(synth.make_weights(shape, 25), DEV)
+    cd = call_to(synth.make_call(shape, 1, 25), DEV)
+    blk = GdnBlock(shape, device=DEV)
+    ws = blk.weights_struct(w)
+    core = torch.zeros(1, shape.value_dim, dtype=torch.bfloat16, device=DEV)
+    lib = abi.load()
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args = [p(cd.x), p(cd.residual), ctypes.byref(ws), p(cd.conv_state), p(cd.ssm_state), p(cd.state_idx)]
+
+    def call(rows, *, x=None, core_ptr=None):
+        a = list(args)
+        if x is not None:
+            a[0] = x
+        return lib.gdn_block_decode(blk.handle, *a, rows, core_ptr if core_ptr is not None else p(core), None)
+
+    assert call(2) == abi.GDN_E_INVALID_ARG and "rows" in abi.gdn_block_last_error(blk.handle)
+    assert call(-1) == abi.GDN_E_INVALID_ARG
+    assert call(1, x=ctypes.c_void_p(0)) == abi.GDN_E_INVALID_ARG and "x is NULL" in abi.gdn_block_last_error(blk.handle)
+    assert call(1, x=ctypes.c_void_p(cd.x.data_ptr() + 2)) == abi.GDN_E_INVALID_ARG
+    assert "aligned" in abi.gdn_block_last_error(blk.handle)
+    torch.cuda.synchronize()
+    before = core.clone()
+    assert call(0) == abi.GDN_OK        # an empty call enqueues nothing
+    torch.cuda.synchronize()
+    assert torch.equal(core, before)
+    assert call(1) == abi.GDN_OK
+    torch.cuda.synchronize()
+    blk.close()
