@@ -60,8 +60,9 @@ class Rotation:
         for i in range(layers):
             w = synth.GdnWeights(**{k: (v.to(dev).clone() if v is not None else None)
                                     for k, v in self.w_cpu.__dict__.items()})
+            packed = self.blk.pack(w)
             c = dict(
-                w=w, ws=self.blk.weights_struct(w),
+                w=w, ws=self.blk.weights_struct(w), packed=packed, wsp=self.blk.packed_struct(w, packed),
                 x=self.call_cpu.x.to(dev).clone(), res=self.call_cpu.residual.to(dev).clone(),
                 conv=self.call_cpu.conv_state.to(dev).clone(), ssm=self.call_cpu.ssm_state.to(dev).clone(),
                 idx=self.call_cpu.state_idx.to(dev).clone(),
@@ -69,35 +70,35 @@ class Rotation:
             self.copies.append(c)
         torch.cuda.synchronize()
 
-    def launch(self, i, rows):
+    def launch(self, i, rows, packed):
         c = self.copies[i % len(self.copies)]
         self.blk.decode(c["x"][:rows], c["res"][:rows], None, c["conv"], c["ssm"], c["idx"][:rows],
-                        c["core"][:rows], weights_struct=c["ws"])
+                        c["core"][:rows], weights_struct=c["wsp"] if packed else c["ws"])
 
-    def graph(self, n, rows, start=0):
+    def graph(self, n, rows, packed):
         import torch
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             for i in range(len(self.copies)):
-                self.launch(i, rows)
+                self.launch(i, rows, packed)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(n):
-                self.launch(start + i, rows)
+                self.launch(i, rows, packed)
         return g
 
-    def time(self, rows, steps, warmup):
+    def time(self, rows, steps, warmup, packed=True):
         """Average µs per launch over exactly `steps` launches (after `warmup`)."""
         import torch
         per = 4 * len(self.copies)           # launches per graph: whole rotations, >= 46 at 12 copies
         while per < 46:
             per += len(self.copies)
-        g = self.graph(per, rows)
+        g = self.graph(per, rows, packed)
         rem = steps % per
-        g_rem = self.graph(rem, rows) if rem else None
+        g_rem = self.graph(rem, rows, packed) if rem else None
         for _ in range(max(1, warmup // per)):
             g.replay()
         torch.cuda.synchronize()
@@ -109,6 +110,9 @@ class Rotation:
             g_rem.replay()
         end.record()
         torch.cuda.synchronize()
+        err = self.blk.check()
+        if err:
+            raise RuntimeError(f"a wait inside the decode gave up (error word {err:#x})")
         return start.elapsed_time(end) * 1000.0 / steps
 
 
@@ -160,6 +164,8 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=960)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -167,6 +173,18 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        # a plain copy of known size, for scaling the HBM byte counters of a profiler run
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": max(1, args.steps)}))
+        return
 
     shape = configs.ALL[args.config]
     sweep_rows = [int(r) for r in args.sweep_rows.split(",") if r]
@@ -179,13 +197,14 @@ def main():
     us = rot.time(args.rows, args.steps, args.warmup)
     algo = configs.algorithmic_bytes(shape, args.rows)
     gbs = algo / (us * 1e-6) / 1e9
-    sweep = {}
+    sweep = {"tiled_weights": {}, "row_major_weights": {}}
     for r in sweep_rows:
-        t = rot.time(r, args.sweep_steps, args.sweep_steps // 4)
         b = configs.algorithmic_bytes(shape, r)
-        sweep[str(r)] = dict(us=round(t, 3), algo_bytes=b, gbs=round(b / (t * 1e-6) / 1e9, 1),
-                             frac=round(b / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
-        log(f"rows {r}: {t:.2f} us/launch")
+        for key, packed in (("tiled_weights", True), ("row_major_weights", False)):
+            t = rot.time(r, args.sweep_steps, args.sweep_steps // 4, packed=packed)
+            sweep[key][str(r)] = dict(us=round(t, 3), algo_bytes=b, gbs=round(b / (t * 1e-6) / 1e9, 1),
+                                      frac=round(b / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+            log(f"rows {r} {key}: {t:.2f} us/launch")
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -219,12 +238,12 @@ def main():
             "value_heads": f"{shape.num_v_heads}x{shape.head_v_dim}",
             "ssm_state": shape.ssm_state_dtype, "in_proj_qkvz": shape.qkvz_format,
             "has_residual": shape.has_residual, "layers_rotated": shape.layers,
-            "state_slots": shape.num_state_slots,
+            "state_slots": shape.num_state_slots, "projection_weights": "tiled copy (gdn_block_pack_weights)",
         },
         "roofline": {
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "algo_bytes_per_launch": algo, "kernel": "gdn_block decode (norm + gemv + gdn launches)",
+            "algo_bytes_per_launch": algo, "kernel": "decode_kernel (the whole block, one launch)",
         },
         "sweep": sweep,
         "cpu_baseline": cpu,

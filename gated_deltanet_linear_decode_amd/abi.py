@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_void_p
+from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_size_t, c_uint32, c_void_p
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn_block.so")
 
@@ -21,7 +21,8 @@ GDN_STATE_F32 = 0
 GDN_STATE_BF16 = 1
 GDN_MAX_ROWS = 16
 
-EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error")
+EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error",
+            "gdn_block_packed_weight_bytes", "gdn_block_pack_weights", "gdn_block_check")
 
 
 class GdnBlockConfig(ctypes.Structure):
@@ -38,6 +39,7 @@ class GdnBlockWeights(ctypes.Structure):
     _fields_ = [
         ("norm_w", c_void_p), ("w_qkvz", c_void_p), ("w_qkvz_scales", c_void_p), ("w_ba", c_void_p),
         ("conv_w", c_void_p), ("A_log", c_void_p), ("dt_bias", c_void_p), ("gated_norm_w", c_void_p),
+        ("w_proj_packed", c_void_p),
     ]
 
 
@@ -51,7 +53,10 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load libgdn_block.so (built in-tree by gated_deltanet_linear_decode_amd.build)."""
+    """Load libgdn_block.so (built in-tree by gated_deltanet_linear_decode_amd.build).
+
+    In a process that also uses torch, import torch first, so that the library binds
+    to the HIP runtime torch has loaded rather than bringing up a second one."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
@@ -66,6 +71,12 @@ def load() -> ctypes.CDLL:
         lib.gdn_block_destroy.restype = None
         lib.gdn_block_last_error.argtypes = [c_void_p]
         lib.gdn_block_last_error.restype = c_char_p
+        lib.gdn_block_packed_weight_bytes.argtypes = [c_void_p]
+        lib.gdn_block_packed_weight_bytes.restype = c_size_t
+        lib.gdn_block_pack_weights.argtypes = [c_void_p, POINTER(GdnBlockWeights), c_void_p, c_void_p]
+        lib.gdn_block_pack_weights.restype = c_int
+        lib.gdn_block_check.argtypes = [c_void_p, POINTER(c_uint32)]
+        lib.gdn_block_check.restype = c_int
         _lib = lib
     return _lib
 
@@ -88,6 +99,25 @@ def gdn_block_decode(handle, x: int, residual: int, weights: GdnBlockWeights, co
                                  state_idx, rows, core_out, stream)
     if rc != GDN_OK:
         raise GdnError(rc, gdn_block_last_error(handle))
+
+
+def gdn_block_packed_weight_bytes(handle) -> int:
+    return int(load().gdn_block_packed_weight_bytes(handle))
+
+
+def gdn_block_pack_weights(handle, weights: GdnBlockWeights, packed: int, stream: int) -> None:
+    rc = load().gdn_block_pack_weights(handle, ctypes.byref(weights), packed, stream)
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(handle))
+
+
+def gdn_block_check(handle) -> int:
+    """The sticky error word of the handle's decodes (read and cleared; synchronous)."""
+    word = c_uint32(0)
+    rc = load().gdn_block_check(handle, ctypes.byref(word))
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(handle))
+    return int(word.value)
 
 
 def gdn_block_destroy(handle) -> None:

@@ -75,7 +75,28 @@ class GdnBlock:
         st.A_log = _check(w.A_log, "A_log", torch.float32, (s.num_v_heads,), d)
         st.dt_bias = _check(w.dt_bias, "dt_bias", torch.bfloat16, (s.num_v_heads,), d)
         st.gated_norm_w = _check(w.gated_norm_w, "gated_norm_w", torch.bfloat16, (s.head_v_dim,), d)
+        st.w_proj_packed = None
         return st
+
+    def pack(self, w, stream=None) -> torch.Tensor:
+        """The tiled projection copy of `w` (a new device tensor), enqueued on `stream`."""
+        st = self.weights_struct(w)
+        out = torch.empty(abi.gdn_block_packed_weight_bytes(self.handle), dtype=torch.uint8, device=self.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        abi.gdn_block_pack_weights(self.handle, st, out.data_ptr(), stream)
+        return out
+
+    def packed_struct(self, w, packed: torch.Tensor) -> abi.GdnBlockWeights:
+        """Weights struct that streams `packed` (from pack()) for the projections."""
+        st = self.weights_struct(w)
+        _check(packed, "packed", torch.uint8, (abi.gdn_block_packed_weight_bytes(self.handle),), self.device)
+        st.w_proj_packed = packed.data_ptr()
+        return st
+
+    def check(self) -> int:
+        """Sticky error word of this handle's decodes (0 = every wait completed)."""
+        return abi.gdn_block_check(self.handle)
 
     def decode(self, x, residual, weights, conv_state, ssm_state, state_idx, core_out, rows=None,
                stream=None, weights_struct=None):

@@ -1,18 +1,37 @@
-// Gated DeltaNet decode block for gfx950: HIP kernels and the C ABI of include/gdn_block.h.
+// Gated DeltaNet decode block for gfx950: one fused decode kernel and the C ABI of
+// include/gdn_block.h.
 //
-// One decode call is three launches on the caller's stream:
-//   norm_kernel   one workgroup per row: h = bf16(x + residual), residual <- h,
-//                 xn = bf16(h * rstd * (1 + w)) into scratch ("sgl-amd-mono PR #89",
-//                 Kernels before and after: the fused residual add + Gemma norm).
-//   gemv_kernel   in_proj_qkvz and in_proj_ba as one skinny GEMM on the bf16 MFMA
-//                 (v_mfma_f32_16x16x32_bf16: 16 weight rows x 16 decode rows per tile).
-//                 K is split over workgroups; the last workgroup of a tile to finish
-//                 (an atomic counter, no waiting) adds the partials in split order, rounds
-//                 to bf16 and runs the tile's epilogue: the causal conv update + SiLU for
-//                 q|k|v channels (rolling the conv state in place), or storing z / b / a.
-//   gdn_kernel    one workgroup per (value head, row): L2 norms, gates, the gated delta
-//                 rule on the head's dk x dv state held in registers, the state store,
-//                 and the gated RMSNorm into the core output.
+// A decode call is ONE launch whose workgroups take one of three roles by block id
+// (the front of a GDN layer as one launch, "sgl-amd-mono PR #89", Modifications; the
+// "GDN block" of "vLLM PR #60833", Details / Launches):
+//
+//   [0, R)            norm: one workgroup per row. h = bf16(x + residual),
+//                     xn = bf16(h * rstd * (1 + w)) published to scratch, then the row is
+//                     counted done and the residual row is rewritten with h. No workgroup
+//                     holds x in LDS; every projection workgroup reads the finished xn
+//                     ("vLLM PR #60833", Details / x without an LDS tile).
+//   [R, R+G)          projection: in_proj_qkvz and in_proj_ba as one skinny GEMM on the
+//                     bf16 MFMA (v_mfma_f32_16x16x32_bf16: 16 weight rows x 16 decode rows
+//                     per step). Each workgroup owns one 16-channel tile and one of S splits
+//                     of K. It issues its weight loads first, then waits for the norm rows,
+//                     multiplies, and publishes its f32 partial sums; then it counts itself
+//                     done for the tile's key-head group (or for the b|a tiles).
+//   [R+G, R+G+R*nv)   recurrence: one workgroup per (row, value head). It loads its
+//                     dk x dv state tile and its conv state and taps first, waits for its
+//                     key-head group and the b|a tiles, adds the split partials of its
+//                     channels in split order and rounds them to bf16 (the projection
+//                     output), runs the causal conv update + SiLU, L2 norms, gates, the gated
+//                     delta rule, the state store and the gated RMSNorm into the core output.
+//                     The q|k conv state of a key head is shared by its r value heads: the
+//                     last of them writes it once the others have read the old rows.
+//
+// Waits only ever target workgroups with lower block ids, which the dispatcher starts
+// first, so every wait ends; each is also bounded and records a sticky error word if it
+// gives up. Data handed from one workgroup to another travels as agent-scope atomic
+// stores (coherent across the XCDs' L2s, one access at a time) followed by a wait for
+// the stores; readers poll counters with agent-scope atomic loads. No device-wide fence
+// is used: on gfx950 one writes back and invalidates a whole L2. Every counter is
+// cleared by the last workgroup that reads it, so the next launch starts from zero.
 //
 // Every reduction runs in a fixed order that does not depend on the row count, so a
 // row's results do not change with the other rows (batch invariance, "sgl-amd-mono PR
@@ -21,7 +40,6 @@
 
 #include <cmath>
 #include <cstdint>
-#include <cstdio>
 #include <cstring>
 #include <string>
 
@@ -32,23 +50,38 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 
-constexpr int kConvW = 4;      // conv width; create() refuses any other
-constexpr int kThreads = 256;  // every kernel runs 4 waves of 64
+constexpr int kConvW = 4;          // conv width; create() refuses any other
+constexpr int kThreads = 256;      // every role runs 4 waves of 64
+constexpr int kLine = 32;          // uint32 words per 128-byte line: one hot counter per line
+// Weight loads each wave keeps in flight (1 KiB each). The window is refilled as it is
+// consumed: enough bytes in flight to keep HBM busy, few enough that the hand-offs between
+// workgroups are not queued behind the whole weight matrix.
+#ifndef GDN_WINDOW
+#define GDN_WINDOW 8
+#endif
+constexpr int kWin = GDN_WINDOW;
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kNormCopies = 8;     // the norm-done counter is kept on 8 lines, polled spread out
 
 // ---------------------------------------------------------------------------------------
 // scalar helpers
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// round-to-nearest-even f32 -> bf16 (inputs are finite)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// f32 -> bf16, round to nearest even: gfx950 converts in hardware (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two values at once: lo in the low half, hi in the high half
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+__device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }  // the bf16 value of f
+
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -66,54 +99,161 @@ __device__ __forceinline__ float block_sum(float v, float* lds) {
   return r;
 }
 
-// cross-workgroup hand-off: coherent single accesses plus a wait for this wave's stores
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
+// cross-workgroup hand-off: single accesses coherent at agent scope
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// this wave's loads have returned and its stores have completed (so a counter bumped
+// after them is seen after them)
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// 16-byte store coherent at agent scope (the vector form of st_agent)
+__device__ __forceinline__ void st_agent16(uint32_t* p, u32x4_t v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+
+// The whole workgroup waits until a counter reaches `target`. Wave 0 polls, backing off
+// between polls so that waiting workgroups do not crowd the counter's memory channel;
+// it gives up after kSpinLimit polls, recording `code`. No memory access after the call
+// is moved above it.
+__device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t target, uint32_t* err, uint32_t code) {
+  if (threadIdx.x < 64) {
+    int it = 0;
+    while (ld_agent(ctr) < target) {
+      __builtin_amdgcn_s_sleep(4);
+      if (++it > kSpinLimit) {
+        __hip_atomic_fetch_or(err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  asm volatile("" ::: "memory");
+}
+
+// In-kernel timeline for profiling builds (-DGDN_TRACE): thread 0 of each workgroup stamps
+// the 100 MHz wall clock at up to kTraceSlots points of its role. Compiled out otherwise.
+#ifdef GDN_TRACE
+constexpr int kTraceSlots = 8;
+constexpr int kTraceBlocks = 8192;
+__device__ unsigned long long g_trace[kTraceBlocks * kTraceSlots];
+#define TRACE_POINT(k)                                                                          \
+  do {                                                                                          \
+    if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks) g_trace[blockIdx.x * kTraceSlots + (k)] = wall_clock64(); \
+  } while (0)
+// slot k <- (XCC id << 16) | hardware id word (CU, SE, ...) of the wave
+#define TRACE_HWID(k)                                                                           \
+  do {                                                                                          \
+    if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks)                                          \
+      g_trace[blockIdx.x * kTraceSlots + (k)] =                                                 \
+          ((unsigned long long)__builtin_amdgcn_s_getreg((3 << 11) | 20) << 32) |              \
+          (unsigned long long)__builtin_amdgcn_s_getreg((31 << 11) | 4);                        \
+  } while (0)
+#else
+#define TRACE_POINT(k) \
+  do {                 \
+  } while (0)
+#define TRACE_HWID(k) \
+  do {                \
+  } while (0)
+#endif
+
+// sync word lines (one 128-byte line each): norm rows done (kNormCopies copies, polled
+// spread out); b|a tile splits done; recurrence workgroups finished; the sticky error
+// word; then per key-head group: tile splits done; then per (row, key-head group): value
+// heads that have read the old q|k conv rows.
+enum { kSyNorm = 0, kSyBa = kNormCopies, kSyExit, kSyError, kSyGroup0 };
+enum : uint32_t { kErrNormWait = 1u, kErrGroupWait = 2u, kErrConvWait = 4u };
+
 // ---------------------------------------------------------------------------------------
-// 1. residual add + Gemma RMSNorm, one workgroup per row
+
+struct Args {
+  // caller tensors
+  const uint16_t* x;         // [R, H]
+  uint16_t* residual;        // [R, H] in/out
+  const uint16_t* norm_w;    // [H]
+  const uint16_t* wq;        // in_proj_qkvz [Nq, H] (row-major path)
+  const uint16_t* wb;        // in_proj_ba [Nb, H] (row-major path)
+  const uint16_t* wpk;       // tiled copy of both (packed path)
+  const uint16_t* conv_w;    // [Cd, 4]
+  uint16_t* conv_state;      // [slots, 3, Cd]
+  void* ssm;                 // [slots, nv, dk, dv] f32 or bf16
+  const int32_t* idx;        // [R]
+  const float* A_log;        // [nv]
+  const uint16_t* dt_bias;   // [nv]
+  const uint16_t* gnw;       // [dv]
+  uint16_t* core;            // [R, nv*dv]
+  // scratch
+  uint16_t* xn;              // [R, H]
+  float* part;               // [R, Nq + Nb, SP] split partials of the projections (SP = S rounded up to 4)
+  uint32_t* sync;            // sync word lines
+  // sizes
+  int H, R, has_res;
+  int T, Tq, Tb, Nq, Nb, S, SP, spw, G, steps;  // tiles, splits, padded splits, K steps per wave, projection WGs
+  int nk, dk, nv, dv, r, GW, Cd, slots;
+  float eps, l2eps, geps;
+};
+
+__device__ __forceinline__ uint32_t* sy(const Args& a, int line) { return a.sync + (size_t)line * kLine; }
+__device__ __forceinline__ int sy_group(int g) { return kSyGroup0 + g; }
+__device__ __forceinline__ int sy_conv(const Args& a, int n, int g) { return kSyGroup0 + a.nk + n * a.nk + g; }
+
+// ---------------------------------------------------------------------------------------
+// role 1: residual add + Gemma RMSNorm of one row
 
 constexpr int kNormMaxChunks = 8;  // 16-byte chunks per thread: H <= 8 * 8 * 256
 
-template <bool HAS_RES>
-__global__ __launch_bounds__(kThreads) void norm_kernel(const uint16_t* __restrict__ x,
-                                                        uint16_t* __restrict__ residual,
-                                                        const uint16_t* __restrict__ w,
-                                                        uint16_t* __restrict__ xn, int H, float eps) {
-  __shared__ float red[4];
-  const int row = blockIdx.x;
-  const int nchunk = H >> 3;
-  const uint4* xp = reinterpret_cast<const uint4*>(x + (size_t)row * H);
-  uint4* rp = reinterpret_cast<uint4*>(residual + (size_t)row * H);
-  uint4 hv[kNormMaxChunks];
+__device__ void norm_role(const Args& a, int row, float* red) {
+  const int H = a.H, nchunk = H >> 3;
+  const uint4* xp = reinterpret_cast<const uint4*>(a.x + (size_t)row * H);
+  uint4* rp = reinterpret_cast<uint4*>(a.residual + (size_t)row * H);
+  const uint4* wp = reinterpret_cast<const uint4*>(a.norm_w);
+  uint4 hv[kNormMaxChunks], wv[kNormMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kNormMaxChunks; ++c) {  // every load of the row is issued up front
+    const int i = threadIdx.x + c * kThreads;
+    if (i < nchunk) hv[c] = xp[i], wv[c] = wp[i];
+  }
+  uint4 rv[kNormMaxChunks];
+  if (a.has_res) {
+#pragma unroll
+    for (int c = 0; c < kNormMaxChunks; ++c) {
+      const int i = threadIdx.x + c * kThreads;
+      if (i < nchunk) rv[c] = rp[i];
+    }
+  }
   float ss = 0.0f;
 #pragma unroll
   for (int c = 0; c < kNormMaxChunks; ++c) {
-    const int idx = threadIdx.x + c * kThreads;
-    if (idx < nchunk) {
-      uint4 a = xp[idx];
-      if (HAS_RES) {
-        const uint4 b = rp[idx];
-        uint32_t* pa = reinterpret_cast<uint32_t*>(&a);
+    const int i = threadIdx.x + c * kThreads;
+    if (i < nchunk) {
+      uint4 v = hv[c];
+      if (a.has_res) {
+        const uint4 b = rv[c];
+        uint32_t* pv = reinterpret_cast<uint32_t*>(&v);
         const uint32_t* pb = reinterpret_cast<const uint32_t*>(&b);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint16_t lo = f2bf(bf2f((uint16_t)pa[q]) + bf2f((uint16_t)pb[q]));
-          const uint16_t hi = f2bf(bf2f((uint16_t)(pa[q] >> 16)) + bf2f((uint16_t)(pb[q] >> 16)));
-          pa[q] = pack2(lo, hi);
-        }
+        for (int q = 0; q < 4; ++q)
+          pv[q] = f2bf2(bf2f((uint16_t)pv[q]) + bf2f((uint16_t)pb[q]),
+                        bf2f((uint16_t)(pv[q] >> 16)) + bf2f((uint16_t)(pb[q] >> 16)));
       }
-      hv[c] = a;
-      const uint32_t* ph = reinterpret_cast<const uint32_t*>(&a);
+      hv[c] = v;
+      const uint32_t* ph = reinterpret_cast<const uint32_t*>(&v);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float l = bf2f((uint16_t)ph[q]), h = bf2f((uint16_t)(ph[q] >> 16));
@@ -123,170 +263,121 @@ __global__ __launch_bounds__(kThreads) void norm_kernel(const uint16_t* __restri
     }
   }
   ss = block_sum(ss, red);
-  const float rstd = 1.0f / sqrtf(ss / (float)H + eps);
-  const uint4* wp = reinterpret_cast<const uint4*>(w);
-  uint4* op = reinterpret_cast<uint4*>(xn + (size_t)row * H);
+  TRACE_POINT(1);
+  const float rstd = 1.0f / sqrtf(ss / (float)H + a.eps);
+  uint32_t* op = reinterpret_cast<uint32_t*>(a.xn + (size_t)row * H);
 #pragma unroll
   for (int c = 0; c < kNormMaxChunks; ++c) {
-    const int idx = threadIdx.x + c * kThreads;
-    if (idx < nchunk) {
-      rp[idx] = hv[c];  // each thread rewrites only the residual chunks it read itself
-      const uint4 wv = wp[idx];
+    const int i = threadIdx.x + c * kThreads;
+    if (i < nchunk) {
       const uint32_t* ph = reinterpret_cast<const uint32_t*>(&hv[c]);
-      const uint32_t* pw = reinterpret_cast<const uint32_t*>(&wv);
-      uint4 o;
-      uint32_t* po = reinterpret_cast<uint32_t*>(&o);
+      const uint32_t* pw = reinterpret_cast<const uint32_t*>(&wv[c]);
+      u32x4_t o4;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint16_t lo = f2bf(bf2f((uint16_t)ph[q]) * rstd * (1.0f + bf2f((uint16_t)pw[q])));
-        const uint16_t hi =
-            f2bf(bf2f((uint16_t)(ph[q] >> 16)) * rstd * (1.0f + bf2f((uint16_t)(pw[q] >> 16))));
-        po[q] = pack2(lo, hi);
-      }
-      op[idx] = o;
+      for (int q = 0; q < 4; ++q)
+        o4[q] = f2bf2(bf2f((uint16_t)ph[q]) * rstd * (1.0f + bf2f((uint16_t)pw[q])),
+                      bf2f((uint16_t)(ph[q] >> 16)) * rstd * (1.0f + bf2f((uint16_t)(pw[q] >> 16))));
+      st_agent16(op + 4 * i, o4);
     }
   }
+  TRACE_POINT(2);
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x < kNormCopies && (int)threadIdx.x < a.G) add_agent(sy(a, kSyNorm + threadIdx.x), 1u);
+  // only this workgroup reads the residual row, so it is rewritten after the hand-off;
+  // each thread rewrites only the chunks it read itself
+#pragma unroll
+  for (int c = 0; c < kNormMaxChunks; ++c) {
+    const int i = threadIdx.x + c * kThreads;
+    if (i < nchunk) rp[i] = hv[c];
+  }
+  TRACE_POINT(3);
 }
 
 // ---------------------------------------------------------------------------------------
-// 2. projections on the MFMA, split-K with a last-arriver reduction, conv epilogue
+// role 2: one split of one 16-channel projection tile
 
-struct GemvArgs {
-  const uint16_t* xn;      // [R, H]
-  const uint16_t* wq;      // in_proj_qkvz [Nq, H]
-  const uint16_t* wb;      // in_proj_ba [Nb, H]
-  const int32_t* idx;      // [R]
-  const uint16_t* conv_w;  // [Cd, 4]
-  uint16_t* conv_state;    // [slots, 3, Cd]
-  uint16_t* cbuf;          // [R, Cd]   conv outputs (bf16, after SiLU)
-  uint16_t* zbuf;          // [R, nv*dv]
-  uint16_t* babuf;         // [R, 2*nv] b then a
-  float* part;             // [S, T, 256] split partials
-  unsigned* cnt;           // [T] arrivals per tile, reset by the last arriver
-  int H, R, Tq, T, Nq, Nb;
-  int nk, dk, nv, dv, r, GW, Cd, slots;
-};
-
-__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, bool isq, int ch, int n, float v, int N) {
-  if (n >= a.R || ch >= N) return;
-  const uint16_t yb = f2bf(v);
-  if (isq) {
-    const int g = ch / a.GW, o = ch - g * a.GW;
-    const int two_dk = 2 * a.dk, rdv = a.r * a.dv;
-    if (o < two_dk + rdv) {
-      int cc;
-      if (o < a.dk)
-        cc = g * a.dk + o;
-      else if (o < two_dk)
-        cc = a.nk * a.dk + g * a.dk + (o - a.dk);
-      else
-        cc = 2 * a.nk * a.dk + g * rdv + (o - two_dk);
-      const int slot = a.idx[n];
-      if (slot <= 0 || slot >= a.slots) return;  // pad row: no conv state write
-      uint16_t* st = a.conv_state + (size_t)slot * (kConvW - 1) * a.Cd + cc;
-      const uint16_t* wc = a.conv_w + (size_t)cc * kConvW;
-      uint16_t prev[kConvW - 1];
-      float acc = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kConvW - 1; ++j) {
-        prev[j] = st[(size_t)j * a.Cd];
-        acc = fmaf(bf2f(wc[j]), bf2f(prev[j]), acc);
-      }
-      acc = fmaf(bf2f(wc[kConvW - 1]), bf2f(yb), acc);
-#pragma unroll
-      for (int j = 0; j < kConvW - 2; ++j) st[(size_t)j * a.Cd] = prev[j + 1];
-      st[(size_t)(kConvW - 2) * a.Cd] = yb;
-      a.cbuf[(size_t)n * a.Cd + cc] = f2bf(silu(acc));
-    } else {
-      a.zbuf[(size_t)n * a.nv * a.dv + g * rdv + (o - two_dk - rdv)] = yb;
-    }
-  } else {
-    const int g = ch / (2 * a.r), o = ch - g * 2 * a.r;
-    const int dst = (o < a.r) ? (g * a.r + o) : (a.nv + g * a.r + (o - a.r));
-    a.babuf[(size_t)n * 2 * a.nv + dst] = yb;
-  }
+// weight operand of K step j for this lane: 8 bf16 of row (lane % 16) at k = 32 j + 8 (lane / 16)
+template <bool PACKED>
+__device__ __forceinline__ const u32x4_t* wptr(const Args& a, int t, int j, int lane) {
+  if (PACKED)  // tile t's steps are consecutive 1 KiB blocks, in lane order
+    return reinterpret_cast<const u32x4_t*>(a.wpk + (((size_t)t * a.steps + j) * 64 + lane) * 8);
+  const bool isq = t < a.Tq;
+  const int N = isq ? a.Nq : a.Nb;
+  // rows past the end are clamped to valid memory; their outputs are never stored
+  const int row = min((isq ? t : t - a.Tq) * 16 + (lane & 15), N - 1);
+  return reinterpret_cast<const u32x4_t*>((isq ? a.wq : a.wb) + (size_t)row * a.H + 32 * j + 8 * (lane >> 4));
 }
 
-// grid: (T tiles of 16 output channels, S splits of K); 4 waves each take a quarter of the
-// workgroup's K range. Lane l of a wave: A operand = weight row (l % 16) of the tile,
-// B operand = decode row (l % 16), both at k offset 8 * (l / 16) of each 32-wide step.
-template <int U>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs a) {
-  __shared__ float red[4][256];
-  __shared__ int is_last;
-  const int t = blockIdx.x, s = blockIdx.y, S = gridDim.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+template <bool PACKED>
+__device__ void proj_role(const Args& a, int gb, float (*red)[256]) {
+  const int t = gb / a.S, s = gb - t * a.S;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
   const bool isq = t < a.Tq;
-  const uint16_t* W = isq ? a.wq : a.wb;
-  const int N = isq ? a.Nq : a.Nb;
-  const int row0 = (isq ? t : t - a.Tq) * 16;
-  const int q16 = lane & 15, kg = lane >> 4;
-  // rows past the end of the matrix or past the decode rows are clamped to valid memory;
-  // their MFMA outputs land in tile positions the epilogue never stores
-  const int wrow = min(row0 + q16, N - 1);
-  const int xrow = min(q16, a.R - 1);
-  const int Kw = a.H / (S * 4);
-  const int k0 = (s * 4 + wave) * Kw + 8 * kg;
-  const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(W + (size_t)wrow * a.H + k0);
-  const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(a.xn + (size_t)xrow * a.H + k0);
+  const int nsteps = a.spw;
+  // K step of iteration i: the workgroup's 4 waves read 4 adjacent steps at every i. Each
+  // workgroup starts at its own point of its K range (a function of the tile and split
+  // only), so that the workgroups streaming at the same moment spread over the HBM
+  // channels instead of all reading the same offset of their regions.
+  const int rot = (t * 7 + s * 3) % nsteps;
+  auto step_of = [&](int i) {
+    const int r = i + rot < nsteps ? i + rot : i + rot - nsteps;
+    return (s * nsteps + r) * 4 + wave;
+  };
+
+  // weight window: step i lives in register set i % kWin until consumed
+  u32x4_t w[kWin];
+#pragma unroll
+  for (int u = 0; u < kWin; ++u)
+    if (u < nsteps) w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, step_of(u), lane));
+
+  const int copy = gb % kNormCopies;
+  wait_count(sy(a, kSyNorm + copy), (uint32_t)a.R, sy(a, kSyError), kErrNormWait);
+  TRACE_POINT(1);
+
+  const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
+  const uint16_t* xbase = a.xn + (size_t)xrow * a.H + 8 * (lane >> 4);
+  auto xload = [&](int i) { return *reinterpret_cast<const u32x4_t*>(xbase + 32 * step_of(i)); };
+  u32x4_t x[kWin];
+#pragma unroll
+  for (int u = 0; u < kWin; ++u)
+    if (u < nsteps) x[u] = xload(u);
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int steps = Kw >> 5;
-  for (int st = 0; st < steps; st += U) {
-    u32x4_t wv[U], xv[U];
+  for (int i0 = 0; i0 < nsteps; i0 += kWin) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      wv[u] = __builtin_nontemporal_load(wp + (st + u) * 4);
-      xv[u] = xp[(st + u) * 4];
+    for (int u = 0; u < kWin; ++u) {
+      const int i = i0 + u;
+      if (i < nsteps) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[u]), as_bf16x8(x[u]), acc, 0, 0, 0);
+        if (i + kWin < nsteps) {
+          w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, step_of(i + kWin), lane));
+          x[u] = xload(i + kWin);
+        }
+      }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wv[u]), as_bf16x8(xv[u]), acc, 0, 0, 0);
   }
+  TRACE_POINT(2);
+
   // D layout: lane l holds channels 4 * (l / 16) + i (i = 0..3) of decode row l % 16
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave][i * 64 + lane] = acc[i];
   __syncthreads();
-  const int tid = threadIdx.x;
   const int en = tid >> 4, em = tid & 15;  // this thread's (decode row, channel) of the tile
   const int src = (em & 3) * 64 + (em >> 2) * 16 + en;
-  float v = ((red[0][src] + red[1][src]) + red[2][src]) + red[3][src];
-  if (S > 1) {
-    // Hand the partial to the tile's last workgroup. Partials travel as agent-scope
-    // atomic stores and loads, which are coherent across the XCDs' L2s one access at a
-    // time; the wait below makes them complete before this workgroup's arrival is
-    // counted. (A device-wide fence here would write back and invalidate a whole L2 in
-    // every workgroup.)
-    store_agent(&a.part[((size_t)s * a.T + t) * 256 + tid], v);
-    wait_stores();
-    __syncthreads();
-    if (tid == 0)
-      is_last = __hip_atomic_fetch_add(&a.cnt[t], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                (unsigned)(S - 1);
-    __syncthreads();
-    if (!is_last) return;
-    v = 0.0f;
-    for (int q = 0; q < S; ++q) v += load_agent(&a.part[((size_t)q * a.T + t) * 256 + tid]);
-    if (tid == 0) __hip_atomic_store(&a.cnt[t], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  gemv_epilogue(a, isq, row0 + em, en, v, N);
+  const float v = ((red[0][src] + red[1][src]) + red[2][src]) + red[3][src];
+  const int ch = (isq ? t * 16 : a.Nq + (t - a.Tq) * 16) + em;  // channel in [qkvz | ba] order
+  if (en < a.R && (isq || ch < a.Nq + a.Nb))
+    st_agent(&a.part[((size_t)en * (a.Nq + a.Nb) + ch) * a.SP + s], v);
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) add_agent(sy(a, isq ? sy_group(t * 16 / a.GW) : kSyBa), 1u);
+  TRACE_POINT(3);
+  TRACE_HWID(7);
 }
 
 // ---------------------------------------------------------------------------------------
-// 3. L2 norms, gates, gated delta rule, gated RMSNorm; one workgroup per (value head, row)
-
-struct GdnArgs {
-  const int32_t* idx;       // [R]
-  const uint16_t* cbuf;     // [R, Cd]
-  const uint16_t* zbuf;     // [R, nv*dv]
-  const uint16_t* babuf;    // [R, 2*nv]
-  const float* A_log;       // [nv]
-  const uint16_t* dt_bias;  // [nv]
-  const uint16_t* gnw;      // [dv]
-  void* ssm;                // [slots, nv, dk, dv]
-  uint16_t* core;           // [R, nv*dv]
-  int nk, nv, r, Cd, slots;
-  float l2eps, geps;
-};
+// role 3: projection sums, conv, L2 norms, gates, gated delta rule and gated RMSNorm of
+// one (row, value head)
 
 template <typename ST>
 struct StateIO;
@@ -311,119 +402,273 @@ struct StateIO<uint16_t> {
   }
   static __device__ __forceinline__ void store(void* base, size_t off, const float* v) {
     uint2 q;
-    q.x = pack2(f2bf(v[0]), f2bf(v[1]));
-    q.y = pack2(f2bf(v[2]), f2bf(v[3]));
+    q.x = f2bf2(v[0], v[1]);
+    q.y = f2bf2(v[2], v[3]);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off) = q;
   }
 };
 
-template <int DK, int DV, typename ST>
-__global__ __launch_bounds__(kThreads) void gdn_kernel(GdnArgs a) {
+struct RecShared {
+  float qs[128], ks[128], vs[128], zs[128], dl[128];
+  float red[1024], red2[1024];  // [row group][column], row groups x dv = 1024 for every head size
+  float scal[8];
+  float bsum[4];
+};
+
+// one conv channel: the three previous raw inputs and the four taps, loaded ahead
+struct ConvIn {
+  uint16_t prev[kConvW - 1];
+  uint16_t w[kConvW];
+  int cc;
+};
+
+__device__ __forceinline__ void conv_load(const Args& a, int slot, int cc, ConvIn& c) {
+  c.cc = cc;
+  const uint16_t* st = a.conv_state + (size_t)slot * (kConvW - 1) * a.Cd + cc;
+#pragma unroll
+  for (int j = 0; j < kConvW - 1; ++j) c.prev[j] = st[(size_t)j * a.Cd];
+  const uint2 w4 = *reinterpret_cast<const uint2*>(a.conv_w + (size_t)cc * kConvW);
+  c.w[0] = (uint16_t)w4.x, c.w[1] = (uint16_t)(w4.x >> 16), c.w[2] = (uint16_t)w4.y, c.w[3] = (uint16_t)(w4.y >> 16);
+}
+
+// bf16(SiLU(sum_j w_j window_j)) with the newest input y (a bf16 value)
+__device__ __forceinline__ float conv_out(const ConvIn& c, float y) {
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kConvW - 1; ++j) s = fmaf(bf2f(c.w[j]), bf2f(c.prev[j]), s);
+  s = fmaf(bf2f(c.w[kConvW - 1]), y, s);
+  return rbf(silu(s));
+}
+
+// roll the channel's conv state: drop the oldest input, append y
+__device__ __forceinline__ void conv_store(const Args& a, int slot, const ConvIn& c, float y) {
+  uint16_t* st = a.conv_state + (size_t)slot * (kConvW - 1) * a.Cd + c.cc;
+#pragma unroll
+  for (int j = 0; j < kConvW - 2; ++j) st[(size_t)j * a.Cd] = c.prev[j + 1];
+  st[(size_t)(kConvW - 2) * a.Cd] = f2bf(y);
+}
+
+// The split partials of one channel of row n sit next to each other (SP <= 8 floats), so
+// one or two 16-byte loads fetch them. Plain loads are safe here: a partial line holds
+// channels of one key-head group (or of the b|a tiles) of one row only, nothing reads it
+// before that group's counter completes, and caches start each launch clean.
+constexpr int kMaxSplits = 8;
+struct Partials {
+  f32x4_t p[2];
+};
+__device__ __forceinline__ Partials proj_load(const Args& a, int n, int ch) {
+  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.part + ((size_t)n * (a.Nq + a.Nb) + ch) * a.SP);
+  Partials r;
+  r.p[0] = src[0];
+  if (a.SP > 4) r.p[1] = src[1];
+  return r;
+}
+// ... added in split order and rounded to bf16: the channel's projection output
+__device__ __forceinline__ float proj_sum(const Args& a, const Partials& r) {
+  float v = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kMaxSplits; ++q)
+    if (q < a.S) v += r.p[q >> 2][q & 3];
+  return rbf(v);
+}
+
+template <int DK, typename ST>
+__device__ void rec_role(const Args& a, int rb, RecShared& sh) {
+  constexpr int DV = DK;
   constexpr int NCQ = DV / 4;          // column quads
   constexpr int NRG = kThreads / NCQ;  // row groups
   constexpr int RPT = DK / NRG;        // state rows per thread
-  static_assert(NRG * NCQ == kThreads && RPT * NRG == DK, "tile shape");
-  __shared__ float qs[DK], ks[DK];
-  __shared__ float red[NRG][DV];
-  __shared__ float vec[DV];
-  __shared__ float scal[4];
-  __shared__ float bsum[4];
-
-  const int h = blockIdx.x, n = blockIdx.y, tid = threadIdx.x;
+  static_assert(NRG * NCQ == kThreads && RPT * NRG == DK && NRG * DV == 1024 && DK <= 128, "tile shape");
+  const int n = rb / a.nv, h = rb - n * a.nv, tid = threadIdx.x;
+  const int kap = h / a.r, hh = h - kap * a.r;
+  const bool qk_owner = hh == a.r - 1;  // writes the key head's q|k conv state
   const int slot = a.idx[n];
-  uint16_t* core = a.core + (size_t)n * a.nv * DV + (size_t)h * DV;
-  if (slot <= 0 || slot >= a.slots) {  // pad row: a zero core row, no state touched
-    for (int j = tid; j < DV; j += kThreads) core[j] = 0;
-    return;
-  }
-  const int kap = h / a.r;
+  const bool valid = slot > 0 && slot < a.slots;
   const int cq = tid % NCQ, rg = tid / NCQ;
-  const size_t sbase = (((size_t)slot * a.nv + h) * DK) * DV + 4 * cq;
+  const size_t sbase = (((size_t)(valid ? slot : 0) * a.nv + h) * DK) * DV + 4 * cq;
 
+  // everything that does not depend on this launch's projections is loaded first
   float S[RPT][4];
+  ConvIn c0, c1;  // threads < DK: q and k channel; threads 128.. 128+DV: v channel (c0)
+  const bool qk_thread = tid < DK, v_thread = tid >= 128 && tid < 128 + DV;
+  if (valid) {
 #pragma unroll
-  for (int m = 0; m < RPT; ++m) StateIO<ST>::load(a.ssm, sbase + (size_t)(rg + NRG * m) * DV, S[m]);
-
-  const uint16_t* crow = a.cbuf + (size_t)n * a.Cd;
-  for (int i = tid; i < DK; i += kThreads) {
-    qs[i] = bf2f(crow[kap * DK + i]);
-    ks[i] = bf2f(crow[a.nk * DK + kap * DK + i]);
-  }
-  __syncthreads();
-  if (tid < 64) {
-    float sq = 0.0f;
-    for (int i = tid; i < DK; i += 64) sq = fmaf(qs[i], qs[i], sq);
-    sq = wave_sum(sq);
-    if (tid == 0) scal[0] = sq;
-  } else if (tid < 128) {
-    float sk = 0.0f;
-    for (int i = tid - 64; i < DK; i += 64) sk = fmaf(ks[i], ks[i], sk);
-    sk = wave_sum(sk);
-    if (tid == 64) scal[1] = sk;
-  } else if (tid == 128) {
-    const uint16_t* ba = a.babuf + (size_t)n * 2 * a.nv;
-    const float b = bf2f(ba[h]);
-    const float x = bf2f(ba[a.nv + h]) + bf2f(a.dt_bias[h]);
-    const float sp = x > 20.0f ? x : log1pf(expf(x));
-    scal[2] = expf(-expf(a.A_log[h]) * sp);  // exp(g)
-    scal[3] = 1.0f / (1.0f + expf(-b));       // beta
-  }
-  __syncthreads();
-  const float qscale = (1.0f / sqrtf(scal[0] + a.l2eps)) * (1.0f / sqrtf((float)DK));
-  const float kscale = 1.0f / sqrtf(scal[1] + a.l2eps);
-  const float decay = scal[2], beta = scal[3];
-
-  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const float kh = ks[rg + NRG * m] * kscale;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      S[m][c] *= decay;
-      part[c] = fmaf(S[m][c], kh, part[c]);
+    for (int m = 0; m < RPT; ++m) StateIO<ST>::load(a.ssm, sbase + (size_t)(rg + NRG * m) * DV, S[m]);
+    if (qk_thread) {
+      conv_load(a, slot, kap * DK + tid, c0);
+      conv_load(a, slot, a.nk * DK + kap * DK + tid, c1);
+    } else if (v_thread) {
+      conv_load(a, slot, 2 * a.nk * DK + h * DV + (tid - 128), c0);
     }
   }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) red[rg][4 * cq + c] = part[c];
-  __syncthreads();
-  if (tid < DV) {
-    float u = 0.0f;
-#pragma unroll
-    for (int q = 0; q < NRG; ++q) u += red[q][tid];
-    const float v = bf2f(crow[2 * a.nk * DK + h * DV + tid]);
-    vec[tid] = beta * (v - u);
+  const float alog = a.A_log[h], dtb = bf2f(a.dt_bias[h]);
+  const float gw = tid < DV ? bf2f(a.gnw[tid]) : 0.0f;
+  if (valid && !qk_owner) {
+    // the old q|k conv rows are in registers: let the owner overwrite them
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) add_agent(sy(a, sy_conv(a, n, kap)), 1u);
   }
-  __syncthreads();
-  float d[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) d[c] = vec[4 * cq + c], part[c] = 0.0f;
-#pragma unroll
-  for (int m = 0; m < RPT; ++m) {
-    const int i = rg + NRG * m;
-    const float kh = ks[i] * kscale, qh = qs[i] * qscale;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      S[m][c] = fmaf(kh, d[c], S[m][c]);
-      part[c] = fmaf(S[m][c], qh, part[c]);
+
+  // every recurrence workgroup waits, pad rows included (see the counter clearing below)
+  wait_count(sy(a, sy_group(kap)), (uint32_t)(a.GW / 16 * a.S), sy(a, kSyError), kErrGroupWait);
+  wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.S), sy(a, kSyError), kErrGroupWait);
+  TRACE_POINT(1);
+
+  uint16_t* core = a.core + (size_t)n * a.nv * DV + (size_t)h * DV;
+  uint32_t exit_ticket = 0;
+  if (valid) {
+    const int gbase = kap * a.GW;
+    // each thread loads the partials of up to two channels, all splits at once
+    const int j = tid - 128;
+    const int ch0 = qk_thread ? gbase + tid : v_thread ? gbase + 2 * DK + hh * DV + j : -1;
+    const int ch1 = qk_thread ? gbase + DK + tid : v_thread ? gbase + 2 * DK + a.r * DV + hh * DV + j : -1;
+    Partials p0, p1, pg;
+    if (ch0 >= 0) p0 = proj_load(a, n, ch0), p1 = proj_load(a, n, ch1);
+    // the two gates are independent chains: thread 64 takes b, thread 65 takes a
+    if (tid == 64 || tid == 65) pg = proj_load(a, n, a.Nq + kap * 2 * a.r + (tid - 64) * a.r + hh);
+    // past every wait of this workgroup: count it (loads complete in issue order, so the
+    // atomic goes after this wave's loads to keep its latency off their path)
+    if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
+    TRACE_POINT(5);
+    float yq = 0.0f, yk = 0.0f;  // this thread's q and k projection outputs (bf16 values)
+    if (qk_thread) {
+      yq = proj_sum(a, p0);
+      yk = proj_sum(a, p1);
+      sh.qs[tid] = conv_out(c0, yq);
+      sh.ks[tid] = conv_out(c1, yk);
+    } else if (v_thread) {
+      const float yv = proj_sum(a, p0);
+      sh.vs[j] = conv_out(c0, yv);
+      sh.zs[j] = proj_sum(a, p1);
+      conv_store(a, slot, c0, yv);
     }
-    StateIO<ST>::store(a.ssm, sbase + (size_t)i * DV, S[m]);
-  }
+    if (tid == 64) {
+      sh.scal[3] = __builtin_amdgcn_rcpf(1.0f + __expf(-proj_sum(a, pg)));  // beta = sigmoid(b)
+    } else if (tid == 65) {
+      const float x = proj_sum(a, pg) + dtb;
+      const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
+      sh.scal[2] = __expf(-__expf(alog) * sp);  // exp(g), g = -exp(A_log) softplus(a + dt_bias)
+    }
+    __syncthreads();
+    TRACE_POINT(2);
+    // squared norms of q and k and their dot product, over the key head dim
+    if (tid < 64) {
+      float sq = 0.0f, sk = 0.0f, kq = 0.0f;
+      for (int i = tid; i < DK; i += 64) {
+        sq = fmaf(sh.qs[i], sh.qs[i], sq);
+        sk = fmaf(sh.ks[i], sh.ks[i], sk);
+        kq = fmaf(sh.ks[i], sh.qs[i], kq);
+      }
+      sq = wave_sum(sq), sk = wave_sum(sk), kq = wave_sum(kq);
+      if (tid == 0) sh.scal[0] = sq, sh.scal[1] = sk, sh.scal[4] = kq;
+    }
+    __syncthreads();
+    TRACE_POINT(6);
+    const float qscale = (1.0f / sqrtf(sh.scal[0] + a.l2eps)) * (1.0f / sqrtf((float)DK));
+    const float kscale = 1.0f / sqrtf(sh.scal[1] + a.l2eps);
+    const float decay = sh.scal[2], beta = sh.scal[3];
+    const float kq = sh.scal[4] * kscale * qscale;  // (normalised k) . (normalised, scaled q)
+
+    // One pass over the old state S: u = S^T k and w = S^T q. With the decay folded in,
+    // the updated state S' = e^g S + k d^T, d = beta (v - e^g u), reads out
+    // o = S'^T q = e^g w + d (k . q); the update itself follows the output.
+    float pu[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int c = 0; c < 4; ++c) red[rg][4 * cq + c] = part[c];
-  __syncthreads();
-  float ob = 0.0f;
-  if (tid < DV) {
-    float o = 0.0f;
+    for (int m = 0; m < RPT; ++m) {
+      const int i = rg + NRG * m;
+      const float kh = sh.ks[i] * kscale, qh = sh.qs[i] * qscale;
 #pragma unroll
-    for (int q = 0; q < NRG; ++q) o += red[q][tid];
-    ob = bf2f(f2bf(o));
+      for (int c = 0; c < 4; ++c) {
+        pu[c] = fmaf(S[m][c], kh, pu[c]);
+        pw[c] = fmaf(S[m][c], qh, pw[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sh.red[rg * DV + 4 * cq + c] = pu[c], sh.red2[rg * DV + 4 * cq + c] = pw[c];
+    __syncthreads();
+    float ob = 0.0f;
+    if (tid < DV) {
+      float u = 0.0f, w = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NRG; ++q) u += sh.red[q * DV + tid], w += sh.red2[q * DV + tid];
+      const float d = beta * (sh.vs[tid] - decay * u);
+      sh.dl[tid] = d;
+      ob = rbf(fmaf(d, kq, decay * w));
+    }
+    const float ss = block_sum(tid < DV ? ob * ob : 0.0f, sh.bsum);  // its barriers publish dl
+    TRACE_POINT(7);
+    const float rstd = 1.0f / sqrtf(ss / (float)DV + a.geps);
+    if (tid < DV) core[tid] = f2bf(ob * rstd * gw * silu(sh.zs[tid]));
+    float d[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) d[c] = sh.dl[4 * cq + c];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const float kh = sh.ks[rg + NRG * m] * kscale;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S[m][c] = fmaf(decay, S[m][c], kh * d[c]);
+      StateIO<ST>::store(a.ssm, sbase + (size_t)(rg + NRG * m) * DV, S[m]);
+    }
+    TRACE_POINT(3);
+
+    if (qk_owner) {
+      // the key head's other value heads have read the old q|k conv rows once they are counted
+      if (a.r > 1) wait_count(sy(a, sy_conv(a, n, kap)), (uint32_t)(a.r - 1), sy(a, kSyError), kErrConvWait);
+      if (qk_thread) {
+        conv_store(a, slot, c0, yq);
+        conv_store(a, slot, c1, yk);
+      }
+      if (tid == 0 && a.r > 1) st_agent(sy(a, sy_conv(a, n, kap)), 0u);
+    }
+  } else {
+    if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
+    for (int j = tid; j < DV; j += kThreads) core[j] = 0;  // pad row: a zero core row
   }
-  const float ss = block_sum(tid < DV ? ob * ob : 0.0f, bsum);
-  const float rstd = 1.0f / sqrtf(ss / (float)DV + a.geps);
-  if (tid < DV) {
-    const float z = bf2f(a.zbuf[(size_t)n * a.nv * DV + (size_t)h * DV + tid]);
-    core[tid] = f2bf(ob * rstd * bf2f(a.gnw[tid]) * silu(z));
+
+  // The last recurrence workgroup past its waits clears the counters for the next launch:
+  // by then every projection tile has been counted (each group and the b|a tiles had a
+  // waiter), so every projection workgroup is past its norm wait, and no recurrence
+  // workgroup reads a counter again (the q|k conv counter is cleared by its owner).
+  if (tid == 128 && exit_ticket == (uint32_t)(a.R * a.nv - 1)) {
+    for (int c = 0; c < kNormCopies; ++c) st_agent(sy(a, kSyNorm + c), 0u);
+    st_agent(sy(a, kSyBa), 0u);
+    for (int g = 0; g < a.nk; ++g) st_agent(sy(a, sy_group(g)), 0u);
+    st_agent(sy(a, kSyExit), 0u);
   }
+  TRACE_POINT(4);
+}
+
+// ---------------------------------------------------------------------------------------
+
+template <bool PACKED, int DK, typename ST>
+__global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
+  __shared__ union {
+    float red[4][256];
+    RecShared rec;
+  } sh;
+  const int b = blockIdx.x;
+  TRACE_POINT(0);
+  if (b < a.R) {
+    norm_role(a, b, sh.red[0]);
+  } else if (b < a.R + a.G) {
+    proj_role<PACKED>(a, b - a.R, sh.red);
+  } else {
+    rec_role<DK, ST>(a, b - a.R - a.G, sh.rec);
+  }
+}
+
+// tiled copy of [in_proj_qkvz; in_proj_ba]: block (t, j) = 64 lanes x 16 bytes, lane l
+// holding row 16 t + l % 16 at k = 32 j + 8 (l / 16); rows past the end are zero
+__global__ __launch_bounds__(64) void pack_kernel(const uint16_t* __restrict__ wq, const uint16_t* __restrict__ wb,
+                                                  uint16_t* __restrict__ out, int H, int Tq, int Nq, int Nb) {
+  const int j = blockIdx.x, t = blockIdx.y, l = threadIdx.x;
+  const bool isq = t < Tq;
+  const int row = (isq ? t : t - Tq) * 16 + (l & 15);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (row < (isq ? Nq : Nb))
+    v = *reinterpret_cast<const uint4*>((isq ? wq : wb) + (size_t)row * H + 32 * j + 8 * (l >> 4));
+  *reinterpret_cast<uint4*>(out + (((size_t)t * (H / 32) + j) * 64 + l) * 8) = v;
 }
 
 }  // namespace
@@ -434,14 +679,11 @@ __global__ __launch_bounds__(kThreads) void gdn_kernel(GdnArgs a) {
 struct gdn_block {
   gdn_block_config cfg;
   int device;
-  int nq, nb, cd, tq, t, splits, unroll;
+  int nq, nb, cd, tq, tb, t, splits, spw, steps, sync_words;
   void* scratch;
   uint16_t* xn;
   float* part;
-  unsigned* cnt;
-  uint16_t* cbuf;
-  uint16_t* zbuf;
-  uint16_t* babuf;
+  uint32_t* sync;
   std::string err;
 };
 
@@ -483,17 +725,21 @@ int fail(gdn_block* b, int code, const std::string& msg) {
   return code;
 }
 
-template <int U>
-void launch_gemv(const gdn_block* b, const GemvArgs& ga, hipStream_t st) {
-  hipLaunchKernelGGL(gemv_kernel<U>, dim3(b->t, b->splits), dim3(kThreads), 0, st, ga);
+template <bool PACKED, int DK>
+void launch_dk(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
+  if (b->cfg.ssm_state_dtype == GDN_STATE_F32)
+    hipLaunchKernelGGL((decode_kernel<PACKED, DK, float>), dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<PACKED, DK, uint16_t>), dim3(grid), dim3(kThreads), 0, st, a);
 }
 
-template <int D>
-void launch_gdn_d(const gdn_block* b, const GdnArgs& ga, int rows, hipStream_t st) {
-  if (b->cfg.ssm_state_dtype == GDN_STATE_F32)
-    hipLaunchKernelGGL((gdn_kernel<D, D, float>), dim3(b->cfg.num_v_heads, rows), dim3(kThreads), 0, st, ga);
-  else
-    hipLaunchKernelGGL((gdn_kernel<D, D, uint16_t>), dim3(b->cfg.num_v_heads, rows), dim3(kThreads), 0, st, ga);
+template <bool PACKED>
+void launch(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
+  switch (b->cfg.head_k_dim) {
+    case 32: launch_dk<PACKED, 32>(b, a, grid, st); break;
+    case 64: launch_dk<PACKED, 64>(b, a, grid, st); break;
+    default: launch_dk<PACKED, 128>(b, a, grid, st); break;
+  }
 }
 
 }  // namespace
@@ -517,33 +763,33 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   b->nb = 2 * nv;
   b->cd = 2 * nk * dk + nv * dv;
   b->tq = b->nq / 16;
-  b->t = b->tq + (b->nb + 15) / 16;
-  // K splits: enough workgroups to cover the chip twice, each wave keeping whole 32-wide
-  // steps; the count depends on the shape only, never on the row count
+  b->tb = (b->nb + 15) / 16;
+  b->t = b->tq + b->tb;
+  b->steps = H / 32;
+  // K splits: at least one projection workgroup per compute unit, each wave keeping a
+  // whole number of 32-wide steps. Fewer, longer-streaming workgroups measured better than
+  // more, shorter ones (late-dispatched workgroups stay behind in the memory queues). The
+  // count depends on the shape only, never on the row count.
   int S = 1;
-  while (S < 8 && b->t * S < 512 && H % (4 * 2 * S * 32) == 0) S *= 2;
+  while (S < 8 && b->t * S < 256 && b->steps % (4 * 2 * S) == 0) S *= 2;
   b->splits = S;
-  const int steps = H / (4 * S * 32);
-  b->unroll = steps % 8 == 0 ? 8 : steps % 4 == 0 ? 4 : steps % 2 == 0 ? 2 : 1;
+  b->spw = b->steps / (4 * S);
+  b->sync_words = (kSyGroup0 + nk + cfg->max_rows * nk) * kLine;
 
   const int R = cfg->max_rows;
   size_t off = 0;
-  const size_t o_xn = off;
-  off = align_up(off + (size_t)R * H * 2, 256);
-  const size_t o_part = off;
-  off = align_up(off + (S > 1 ? (size_t)S * b->t * 256 * 4 : 0), 256);
-  const size_t o_cnt = off;
-  off = align_up(off + (size_t)b->t * 4, 256);
-  const size_t o_c = off;
-  off = align_up(off + (size_t)R * b->cd * 2, 256);
-  const size_t o_z = off;
-  off = align_up(off + (size_t)R * nv * dv * 2, 256);
-  const size_t o_ba = off;
-  off = align_up(off + (size_t)R * 2 * nv * 2, 256);
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_xn = take((size_t)R * H * 2);
+  const size_t o_part = take((size_t)(S > 4 ? 8 : 4) * R * (b->nq + b->nb) * 4);
+  const size_t o_sync = take((size_t)b->sync_words * 4);
 
   hipError_t e = hipGetDevice(&b->device);
   if (e == hipSuccess) e = hipMalloc(&b->scratch, off);
-  if (e == hipSuccess) e = hipMemset(static_cast<char*>(b->scratch) + o_cnt, 0, (size_t)b->t * 4);
+  if (e == hipSuccess) e = hipMemset(b->scratch, 0, off);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     g_create_error = std::string("gdn_block_create: HIP error: ") + hipGetErrorString(e);
@@ -554,12 +800,30 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   char* base = static_cast<char*>(b->scratch);
   b->xn = reinterpret_cast<uint16_t*>(base + o_xn);
   b->part = reinterpret_cast<float*>(base + o_part);
-  b->cnt = reinterpret_cast<unsigned*>(base + o_cnt);
-  b->cbuf = reinterpret_cast<uint16_t*>(base + o_c);
-  b->zbuf = reinterpret_cast<uint16_t*>(base + o_z);
-  b->babuf = reinterpret_cast<uint16_t*>(base + o_ba);
+  b->sync = reinterpret_cast<uint32_t*>(base + o_sync);
   g_create_error.clear();
   *out = b;
+  return GDN_OK;
+}
+
+extern "C" size_t gdn_block_packed_weight_bytes(gdn_block_t b) {
+  if (!b) return 0;
+  return (size_t)b->t * 16 * b->cfg.hidden * 2;
+}
+
+extern "C" int gdn_block_pack_weights(gdn_block_t b, const gdn_block_weights* w, void* packed, void* stream) {
+  if (!b) return GDN_E_INVALID_ARG;
+  if (!w || !w->w_qkvz || !w->w_ba || !packed)
+    return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w, w->w_qkvz, w->w_ba and packed must not be NULL");
+  if (!aligned16(w->w_qkvz) || !aligned16(w->w_ba) || !aligned16(packed))
+    return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: pointers must be 16-byte aligned");
+  if (b->cfg.qkvz_format != GDN_FMT_BF16)
+    return fail(b, GDN_E_UNSUPPORTED, "gdn_block_pack_weights: only bf16 in_proj_qkvz is tiled");
+  hipLaunchKernelGGL(pack_kernel, dim3(b->steps, b->t), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(w->w_qkvz), static_cast<const uint16_t*>(w->w_ba),
+                     static_cast<uint16_t*>(packed), b->cfg.hidden, b->tq, b->nq, b->nb);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(b, GDN_E_HIP, std::string("gdn_block_pack_weights: ") + hipGetErrorString(e));
   return GDN_OK;
 }
 
@@ -573,87 +837,93 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
                 "gdn_block_decode: rows must be in 0.." + std::to_string(c.max_rows) + " (got " +
                     std::to_string(rows) + ")");
   if (!w) return fail(b, GDN_E_INVALID_ARG, "gdn_block_decode: weights must not be NULL");
-  const void* ptrs[] = {x, residual, conv_state, ssm_state, state_idx, core_out, w->norm_w, w->w_qkvz,
-                        w->w_ba, w->conv_w, w->A_log, w->dt_bias, w->gated_norm_w};
+  const bool packed = w->w_proj_packed != nullptr;
+  const void* ptrs[] = {x, residual, conv_state, ssm_state, state_idx, core_out, w->norm_w,
+                        packed ? w->w_proj_packed : w->w_qkvz, packed ? w->w_proj_packed : w->w_ba,
+                        w->conv_w, w->A_log, w->dt_bias, w->gated_norm_w};
   const char* names[] = {"x", "residual", "conv_state", "ssm_state", "state_idx", "core_out", "norm_w",
-                         "w_qkvz", "w_ba", "conv_w", "A_log", "dt_bias", "gated_norm_w"};
+                         packed ? "w_proj_packed" : "w_qkvz", packed ? "w_proj_packed" : "w_ba", "conv_w",
+                         "A_log", "dt_bias", "gated_norm_w"};
   for (size_t i = 0; i < sizeof(ptrs) / sizeof(ptrs[0]); ++i) {
     if (!ptrs[i]) return fail(b, GDN_E_INVALID_ARG, std::string("gdn_block_decode: ") + names[i] + " is NULL");
     if (!aligned16(ptrs[i]))
       return fail(b, GDN_E_INVALID_ARG, std::string("gdn_block_decode: ") + names[i] + " is not 16-byte aligned");
   }
   if (rows == 0) return GDN_OK;
+
+  Args a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.residual = static_cast<uint16_t*>(residual);
+  a.norm_w = static_cast<const uint16_t*>(w->norm_w);
+  a.wq = static_cast<const uint16_t*>(w->w_qkvz);
+  a.wb = static_cast<const uint16_t*>(w->w_ba);
+  a.wpk = static_cast<const uint16_t*>(w->w_proj_packed);
+  a.conv_w = static_cast<const uint16_t*>(w->conv_w);
+  a.conv_state = static_cast<uint16_t*>(conv_state);
+  a.ssm = ssm_state;
+  a.idx = state_idx;
+  a.A_log = w->A_log;
+  a.dt_bias = static_cast<const uint16_t*>(w->dt_bias);
+  a.gnw = static_cast<const uint16_t*>(w->gated_norm_w);
+  a.core = static_cast<uint16_t*>(core_out);
+  a.xn = b->xn;
+  a.part = b->part;
+  a.sync = b->sync;
+  a.H = c.hidden;
+  a.R = rows;
+  a.has_res = c.has_residual;
+  a.T = b->t;
+  a.Tq = b->tq;
+  a.Tb = b->tb;
+  a.Nq = b->nq;
+  a.Nb = b->nb;
+  a.S = b->splits;
+  a.SP = b->splits > 4 ? 8 : 4;
+  a.spw = b->spw;
+  a.G = b->t * b->splits;
+  a.steps = b->steps;
+  a.nk = c.num_k_heads;
+  a.dk = c.head_k_dim;
+  a.nv = c.num_v_heads;
+  a.dv = c.head_v_dim;
+  a.r = c.num_v_heads / c.num_k_heads;
+  a.GW = 2 * c.head_k_dim + 2 * a.r * c.head_v_dim;
+  a.Cd = b->cd;
+  a.slots = c.num_state_slots;
+  a.eps = c.norm_eps;
+  a.l2eps = c.l2norm_eps;
+  a.geps = c.gated_norm_eps;
+
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int H = c.hidden;
-
-  if (c.has_residual)
-    hipLaunchKernelGGL(norm_kernel<true>, dim3(rows), dim3(kThreads), 0, st, static_cast<const uint16_t*>(x),
-                       static_cast<uint16_t*>(residual), static_cast<const uint16_t*>(w->norm_w), b->xn, H,
-                       c.norm_eps);
+  const int grid = rows + a.G + rows * c.num_v_heads;
+  if (packed)
+    launch<true>(b, a, grid, st);
   else
-    hipLaunchKernelGGL(norm_kernel<false>, dim3(rows), dim3(kThreads), 0, st, static_cast<const uint16_t*>(x),
-                       static_cast<uint16_t*>(residual), static_cast<const uint16_t*>(w->norm_w), b->xn, H,
-                       c.norm_eps);
-
-  GemvArgs ga;
-  ga.xn = b->xn;
-  ga.wq = static_cast<const uint16_t*>(w->w_qkvz);
-  ga.wb = static_cast<const uint16_t*>(w->w_ba);
-  ga.idx = state_idx;
-  ga.conv_w = static_cast<const uint16_t*>(w->conv_w);
-  ga.conv_state = static_cast<uint16_t*>(conv_state);
-  ga.cbuf = b->cbuf;
-  ga.zbuf = b->zbuf;
-  ga.babuf = b->babuf;
-  ga.part = b->part;
-  ga.cnt = b->cnt;
-  ga.H = H;
-  ga.R = rows;
-  ga.Tq = b->tq;
-  ga.T = b->t;
-  ga.Nq = b->nq;
-  ga.Nb = b->nb;
-  ga.nk = c.num_k_heads;
-  ga.dk = c.head_k_dim;
-  ga.nv = c.num_v_heads;
-  ga.dv = c.head_v_dim;
-  ga.r = c.num_v_heads / c.num_k_heads;
-  ga.GW = 2 * c.head_k_dim + 2 * ga.r * c.head_v_dim;
-  ga.Cd = b->cd;
-  ga.slots = c.num_state_slots;
-  switch (b->unroll) {
-    case 8: launch_gemv<8>(b, ga, st); break;
-    case 4: launch_gemv<4>(b, ga, st); break;
-    case 2: launch_gemv<2>(b, ga, st); break;
-    default: launch_gemv<1>(b, ga, st); break;
-  }
-
-  GdnArgs da;
-  da.idx = state_idx;
-  da.cbuf = b->cbuf;
-  da.zbuf = b->zbuf;
-  da.babuf = b->babuf;
-  da.A_log = w->A_log;
-  da.dt_bias = static_cast<const uint16_t*>(w->dt_bias);
-  da.gnw = static_cast<const uint16_t*>(w->gated_norm_w);
-  da.ssm = ssm_state;
-  da.core = static_cast<uint16_t*>(core_out);
-  da.nk = c.num_k_heads;
-  da.nv = c.num_v_heads;
-  da.r = ga.r;
-  da.Cd = b->cd;
-  da.slots = c.num_state_slots;
-  da.l2eps = c.l2norm_eps;
-  da.geps = c.gated_norm_eps;
-  switch (c.head_k_dim) {
-    case 32: launch_gdn_d<32>(b, da, rows, st); break;
-    case 64: launch_gdn_d<64>(b, da, rows, st); break;
-    default: launch_gdn_d<128>(b, da, rows, st); break;
-  }
+    launch<false>(b, a, grid, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(b, GDN_E_HIP, std::string("gdn_block_decode: launch failed: ") + hipGetErrorString(e));
   return GDN_OK;
 }
+
+extern "C" int gdn_block_check(gdn_block_t b, uint32_t* error_word) {
+  if (!b || !error_word) return GDN_E_INVALID_ARG;
+  uint32_t v = 0;
+  uint32_t* word = b->sync + (size_t)kSyError * kLine;
+  hipError_t e = hipMemcpy(&v, word, 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && v) e = hipMemset(word, 0, 4);
+  if (e != hipSuccess) return fail(b, GDN_E_HIP, std::string("gdn_block_check: ") + hipGetErrorString(e));
+  *error_word = v;
+  return GDN_OK;
+}
+
+#ifdef GDN_TRACE
+// profiling builds only: copy the last launch's per-workgroup timestamps (kTraceSlots per block)
+extern "C" int gdn_block_trace_copy(unsigned long long* host, size_t blocks) {
+  if (blocks > (size_t)kTraceBlocks) blocks = kTraceBlocks;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_trace), blocks * kTraceSlots * sizeof(unsigned long long), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? GDN_OK : GDN_E_HIP;
+}
+#endif
 
 extern "C" void gdn_block_destroy(gdn_block_t b) {
   if (!b) return;

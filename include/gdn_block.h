@@ -44,12 +44,21 @@
  *   state_idx         [rows] int32 in device memory; value head h uses key head h / r
  *   core_out          [rows, nv*dv] bf16
  *
+ * Tiled projection weights (optional, faster): gdn_block_pack_weights writes a copy
+ * of [in_proj_qkvz; in_proj_ba] cut into 16-row tiles whose 32-wide K steps are
+ * stored as consecutive 1 KiB blocks in the operand order of the bf16 matrix cores,
+ * so every load instruction of the projection reads 1 KiB of contiguous memory.
+ * Pass it as w_proj_packed; w_qkvz and w_ba are then not read. The copy is made
+ * once (like the pages' shuffled weight copies made before graph capture, "SGLang
+ * PR #43558", Modifications / Weights) and has the size of the two matrices.
+ *
  * Errors: every function returns GDN_OK (0) or a negative code; the message
  * is kept per handle (gdn_block_last_error). A failed check enqueues nothing.
  */
 #ifndef GDN_BLOCK_H
 #define GDN_BLOCK_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -95,6 +104,7 @@ typedef struct gdn_block_weights {
   const float* A_log;        /* [nv] f32 */
   const void* dt_bias;       /* [nv] bf16 */
   const void* gated_norm_w;  /* [dv] bf16 */
+  const void* w_proj_packed; /* NULL, or the tiled copy from gdn_block_pack_weights */
 } gdn_block_weights;
 
 typedef struct gdn_block* gdn_block_t;
@@ -122,6 +132,23 @@ int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out);
 int gdn_block_decode(gdn_block_t blk, const void* x, void* residual, const gdn_block_weights* w,
                      void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
                      void* core_out, void* stream);
+
+/* Size in bytes of the tiled projection copy (16-row tiles of [in_proj_qkvz;
+ * in_proj_ba], the last tile zero-padded): T * 16 * H * 2 with
+ * T = Nqkvz/16 + ceil(2*nv/16). 0 for a NULL handle. */
+size_t gdn_block_packed_weight_bytes(gdn_block_t blk);
+
+/* Enqueue on `stream` the write of the tiled copy of w->w_qkvz and w->w_ba (bf16,
+ * row-major) into `packed` (device memory of gdn_block_packed_weight_bytes bytes,
+ * 16-byte aligned, caller-owned). Only for GDN_FMT_BF16. */
+int gdn_block_pack_weights(gdn_block_t blk, const gdn_block_weights* w, void* packed, void* stream);
+
+/* Read and clear the handle's sticky error word (synchronous; not for the hot
+ * path). Inside a decode, every wait for another workgroup is bounded; a wait
+ * that gives up sets a bit (1: waiting for the norm rows, 2: waiting for a
+ * key-head group's projection tiles) and lets the launch finish with undefined
+ * outputs. 0 means every decode since the last check completed normally. */
+int gdn_block_check(gdn_block_t blk, uint32_t* error_word);
 
 /* Free the handle and its scratch (NULL is a no-op). Waits for nothing: the
  * caller must make sure no enqueued decode still uses it. */

@@ -33,16 +33,29 @@ def call_to(c: GdnCall, dev) -> GdnCall:
     return GdnCall(**{k: v.to(dev).contiguous() for k, v in c.__dict__.items()})
 
 
-def run_gpu(blk: GdnBlock, shape, wd: GdnWeights, cd: GdnCall, rows=None):
-    """Run one decode on copies of the device inputs; returns CPU tensors."""
+def run_gpu(blk: GdnBlock, shape, wd: GdnWeights, cd: GdnCall, rows=None, packed=None):
+    """Run one decode on copies of the device inputs; returns CPU tensors.
+
+    `packed`: None streams the row-major weights; a tensor from blk.pack() streams
+    the tiled copy. The handle's sticky error word must stay 0."""
     R = cd.x.shape[0] if rows is None else rows
     res = cd.residual.clone()
     conv = cd.conv_state.clone()
     ssm = cd.ssm_state.clone()
     core = torch.full((R, shape.value_dim), float("nan"), dtype=torch.bfloat16, device=cd.x.device)
-    blk.decode(cd.x, res, wd, conv, ssm, cd.state_idx, core)
+    ws = blk.packed_struct(wd, packed) if packed is not None else blk.weights_struct(wd)
+    blk.decode(cd.x, res, None, conv, ssm, cd.state_idx, core, weights_struct=ws)
     torch.cuda.synchronize()
+    assert blk.check() == 0, "a wait inside the decode gave up"
     return dict(core=core.cpu(), residual=res.cpu(), conv_state=conv.cpu(), ssm_state=ssm.cpu())
+
+
+def same_bits(a: dict, b: dict):
+    for k in a:
+        x, y = a[k], b[k]
+        if x.dtype == torch.bfloat16:
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        assert torch.equal(x, y), f"{k} differs between the two weight layouts"
 
 
 def _ulp_bf16(r):

@@ -88,7 +88,8 @@ def test_graph_replay_equals_eager():
     shape = configs.TP8_RANK_BF16.with_(num_state_slots=32, rows=(8,), has_residual=True, pad_rows=True)
     w = weights_to(synth.make_weights(shape, 24), DEV)
     blk = GdnBlock(shape, max_rows=8, device=DEV)
-    ws = blk.weights_struct(w)
+    packed = blk.pack(w)
+    ws = blk.packed_struct(w, packed)
     widths = (8, 1, 3, 8, 2, 5)
     calls = [call_to(synth.make_call(shape, r, 300 + i), DEV) for i, r in enumerate(widths)]
     conv0, ssm0 = calls[0].conv_state.clone(), calls[0].ssm_state.clone()
@@ -134,6 +135,7 @@ def test_graph_replay_equals_eager():
         if rep % 50 == 0:
             note(f"graph replay {rep}: mismatches so far {mismatches}")
     assert mismatches == 0
+    assert blk.check() == 0
     blk.close()
 
 
@@ -166,4 +168,37 @@ def test_decode_rejects_bad_arguments_on_the_host():
     assert torch.equal(core, before)
     assert call(1) == abi.GDN_OK
     torch.cuda.synchronize()
+    blk.close()
+
+
+def test_pack_rejects_bad_arguments():
+    shape = configs.TINY
+    w = weights_to(synth.make_weights(shape, 26), DEV)
+    blk = GdnBlock(shape, device=DEV)
+    ws = blk.weights_struct(w)
+    lib = abi.load()
+    assert abi.gdn_block_packed_weight_bytes(blk.handle) == (shape.n_qkvz // 16 + 1) * 16 * shape.hidden * 2
+    assert lib.gdn_block_pack_weights(blk.handle, ctypes.byref(ws), None, None) == abi.GDN_E_INVALID_ARG
+    out = torch.empty(abi.gdn_block_packed_weight_bytes(blk.handle) + 16, dtype=torch.uint8, device=DEV)
+    assert lib.gdn_block_pack_weights(blk.handle, ctypes.byref(ws), ctypes.c_void_p(out.data_ptr() + 8),
+                                      None) == abi.GDN_E_INVALID_ARG
+    blk.close()
+
+
+def test_repeated_decodes_keep_counters_consistent():
+    """Many back-to-back launches of varying width and pad mix on one handle: every
+    launch must find its hand-off counters cleared by the previous one."""
+    shape = configs.TP8_RANK_F32.with_(num_state_slots=40)
+    w = weights_to(synth.make_weights(shape, 27), DEV)
+    blk = GdnBlock(shape, device=DEV)
+    packed = blk.pack(w)
+    for i, rows in enumerate((16, 1, 7, 16, 3, 1, 12)):
+        cd = call_to(synth.make_call(shape, rows, 400 + i, all_pad=(i == 5)), DEV)
+        a = run_gpu(blk, shape, w, cd, packed=packed)
+        b = run_gpu(blk, shape, w, cd)
+        for k in a:
+            x, y = a[k], b[k]
+            if x.dtype == torch.bfloat16:
+                x, y = x.view(torch.int16), y.view(torch.int16)
+            assert torch.equal(x, y), (rows, k)
     blk.close()
