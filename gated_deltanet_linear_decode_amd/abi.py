@@ -22,7 +22,8 @@ GDN_STATE_BF16 = 1
 GDN_MAX_ROWS = 16
 
 EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error",
-            "gdn_block_packed_weight_bytes", "gdn_block_pack_weights", "gdn_block_check")
+            "gdn_block_packed_weight_bytes", "gdn_block_pack_weights", "gdn_block_check",
+            "gdn_mxfp4_quantize")
 
 
 class GdnBlockConfig(ctypes.Structure):
@@ -77,6 +78,8 @@ def load() -> ctypes.CDLL:
         lib.gdn_block_pack_weights.restype = c_int
         lib.gdn_block_check.argtypes = [c_void_p, POINTER(c_uint32)]
         lib.gdn_block_check.restype = c_int
+        lib.gdn_mxfp4_quantize.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
+        lib.gdn_mxfp4_quantize.restype = c_int
         _lib = lib
     return _lib
 
@@ -118,6 +121,12 @@ def gdn_block_check(handle) -> int:
     if rc != GDN_OK:
         raise GdnError(rc, gdn_block_last_error(handle))
     return int(word.value)
+
+
+def gdn_mxfp4_quantize(x: int, rows: int, cols: int, codes: int, scales: int, stream: int) -> None:
+    rc = load().gdn_mxfp4_quantize(x, rows, cols, codes, scales, stream)
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(None))
 
 
 def gdn_block_destroy(handle) -> None:

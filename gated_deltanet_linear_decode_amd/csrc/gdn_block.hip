@@ -10,12 +10,16 @@
 //                     counted done and the residual row is rewritten with h. No workgroup
 //                     holds x in LDS; every projection workgroup reads the finished xn
 //                     ("vLLM PR #60833", Details / x without an LDS tile).
+//                     With MXFP4 in_proj_qkvz the row is also quantised to MXFP4 (codes +
+//                     one e8m0 scale per 32) into a second scratch image.
 //   [R, R+G)          projection: in_proj_qkvz and in_proj_ba as one skinny GEMM on the
-//                     bf16 MFMA (v_mfma_f32_16x16x32_bf16: 16 weight rows x 16 decode rows
-//                     per step). Each workgroup owns one 16-channel tile and one of S splits
-//                     of K. It issues its weight loads first, then waits for the norm rows,
-//                     multiplies, and publishes its f32 partial sums; then it counts itself
-//                     done for the tile's key-head group (or for the b|a tiles).
+//                     matrix cores: bf16 weights on v_mfma_f32_16x16x32_bf16, MXFP4 weights
+//                     on v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 x fp4 with per-32 scales);
+//                     16 weight rows x 16 decode rows per instruction. Each workgroup owns
+//                     one 16-channel tile and one split of K. It issues its weight loads
+//                     first, then waits for the norm rows, multiplies, and publishes its f32
+//                     partial sums; then it counts itself done for the tile's key-head group
+//                     (or for the b|a tiles).
 //   [R+G, R+G+R*nv)   recurrence: one workgroup per (row, value head). It loads its
 //                     dk x dv state tile and its conv state and taps first, waits for its
 //                     key-head group and the b|a tiles, adds the split partials of its
@@ -38,6 +42,7 @@
 // #89", Kernel checks).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -52,6 +57,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 
 constexpr int kConvW = 4;          // conv width; create() refuses any other
 constexpr int kThreads = 256;      // every role runs 4 waves of 64
@@ -189,7 +195,11 @@ struct Args {
   const uint16_t* norm_w;    // [H]
   const uint16_t* wq;        // in_proj_qkvz [Nq, H] (row-major path)
   const uint16_t* wb;        // in_proj_ba [Nb, H] (row-major path)
-  const uint16_t* wpk;       // tiled copy of both (packed path)
+  const uint16_t* wpk;       // tiled copy: in_proj_qkvz tiles (bf16, or MXFP4 codes)
+  const uint16_t* wpk_ba;    // tiled copy: in_proj_ba tiles (bf16)
+  const uint8_t* wqc;        // MXFP4 in_proj_qkvz codes [Nq, H/2] (row-major path)
+  const uint8_t* wqs;        // MXFP4 in_proj_qkvz scales [Nq, H/32] (row-major path)
+  const uint32_t* wpk_sc;    // tiled copy: MXFP4 scales, one dword per lane per 4 K steps
   const uint16_t* conv_w;    // [Cd, 4]
   uint16_t* conv_state;      // [slots, 3, Cd]
   void* ssm;                 // [slots, nv, dk, dv] f32 or bf16
@@ -200,11 +210,14 @@ struct Args {
   uint16_t* core;            // [R, nv*dv]
   // scratch
   uint16_t* xn;              // [R, H]
+  uint32_t* xq;              // MXFP4 image of xn: codes [R, H/2] bytes
+  uint32_t* xqs;             // MXFP4 image of xn: scales [R, H/32] bytes, grouped per 4 K steps
   float* part;               // [R, Nq + Nb, SP] split partials of the projections (SP = S rounded up to 4)
   uint32_t* sync;            // sync word lines
   // sizes
   int H, R, has_res;
   int T, Tq, Tb, Nq, Nb, S, SP, spw, G, steps;  // tiles, splits, padded splits, K steps per wave, projection WGs
+  int Sb, spwb, Gq, ups;     // b|a tile splits and steps per wave; qkvz workgroups; MXFP4 units per split
   int nk, dk, nv, dv, r, GW, Cd, slots;
   float eps, l2eps, geps;
 };
@@ -218,6 +231,40 @@ __device__ __forceinline__ int sy_conv(const Args& a, int n, int g) { return kSy
 
 constexpr int kNormMaxChunks = 8;  // 16-byte chunks per thread: H <= 8 * 8 * 256
 
+// MXFP4 quantisation of one 32-element block held by 4 consecutive lanes, 8 bf16 each
+// (dwords in element order, the even element in the low half). The block exponent is the
+// smallest e with max|x| <= 6 * 2^e, clamped below at -126; with max|x| = M * 2^E
+// (1 <= M < 2) that is E - 2, plus 1 when M > 1.5. Each x / 2^e (exact: a power-of-two
+// scaling) is rounded to the nearest e2m1 value, ties to the even code: the code counts
+// the rounding boundaries 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 that |x| / 2^e passes (a
+// boundary that is a tie belongs to the even side). A zero code carries no sign.
+// ("vLLM PR #60833", Details / MoE: dynamic MXFP4 in 1x32 blocks with RCEIL scales.)
+// All 4 lanes of the block must be active. Returns the 8 codes (element 8 j + q in nibble
+// q); the scale byte e + 127 goes to `ebyte`.
+__device__ __forceinline__ uint32_t mx_quant8(const uint32_t* v, uint32_t& ebyte) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) m = max(m, max(v[q] & 0x7fffu, (v[q] >> 16) & 0x7fffu));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
+  const int ef = (int)(m >> 7);
+  const int e = ef == 0 ? -126 : max(-126, ef - 129 + ((m & 0x7fu) > 0x40u ? 1 : 0));
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
+  uint32_t codes = 0;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t b = (q & 1) ? (v[q >> 1] >> 16) : (v[q >> 1] & 0xffffu);
+    const float x = bf2f((uint16_t)(b & 0x7fffu)) * inv;
+    uint32_t c = (uint32_t)(x > 0.25f) + (uint32_t)(x >= 0.75f) + (uint32_t)(x > 1.25f) + (uint32_t)(x >= 1.75f) +
+                 (uint32_t)(x > 2.5f) + (uint32_t)(x >= 3.5f) + (uint32_t)(x > 5.0f);
+    if ((b & 0x8000u) && c) c |= 8u;
+    codes |= c << (4 * q);
+  }
+  ebyte = (uint32_t)(e + 127);
+  return codes;
+}
+
+template <bool MX>
 __device__ void norm_role(const Args& a, int row, float* red) {
   const int H = a.H, nchunk = H >> 3;
   const uint4* xp = reinterpret_cast<const uint4*>(a.x + (size_t)row * H);
@@ -278,6 +325,19 @@ __device__ void norm_role(const Args& a, int row, float* red) {
         o4[q] = f2bf2(bf2f((uint16_t)ph[q]) * rstd * (1.0f + bf2f((uint16_t)pw[q])),
                       bf2f((uint16_t)(ph[q] >> 16)) * rstd * (1.0f + bf2f((uint16_t)(pw[q] >> 16))));
       st_agent16(op + 4 * i, o4);
+      if (MX) {
+        // H is a multiple of 512, so a wave's 64 chunks are all in range together
+        uint32_t v[4] = {o4[0], o4[1], o4[2], o4[3]}, eb;
+        st_agent(a.xq + (size_t)row * (H >> 3) + i, mx_quant8(v, eb));
+        // The wave's 64 chunks are the 16 blocks of 4 K steps of 128: block 4 s + kb holds
+        // K quarter kb of step s. Scales are stored per (4 steps, quarter kb) as one dword,
+        // byte s, the operand a projection lane of quarter kb reads for 4 steps at once.
+        const int lane = threadIdx.x & 63, kb = (lane >> 2) & 3;
+        uint32_t d = 0;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) d |= (uint32_t)__shfl((int)eb, 16 * st + 4 * kb, 64) << (8 * st);
+        if (lane < 16 && (lane & 3) == 0) st_agent(a.xqs + (size_t)row * (H >> 7) + 4 * (i >> 6) + kb, d);
+      }
     }
   }
   TRACE_POINT(2);
@@ -297,24 +357,45 @@ __device__ void norm_role(const Args& a, int row, float* red) {
 // ---------------------------------------------------------------------------------------
 // role 2: one split of one 16-channel projection tile
 
-// weight operand of K step j for this lane: 8 bf16 of row (lane % 16) at k = 32 j + 8 (lane / 16)
+// f32 accumulator of a 16-channel tile -> the tile's split partials, then the tile counts
+// itself done for its key-head group (or for the b|a tiles). D layout of the 16x16 MFMAs:
+// lane l holds channels 4 (l / 16) + i (i = 0..3) of decode row l % 16.
+__device__ __forceinline__ void publish_tile(const Args& a, int t, int s, f32x4_t acc, float (*red)[256]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
+  const bool isq = t < a.Tq;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][i * 64 + lane] = acc[i];
+  __syncthreads();
+  const int en = tid >> 4, em = tid & 15;  // this thread's (decode row, channel) of the tile
+  const int src = (em & 3) * 64 + (em >> 2) * 16 + en;
+  const float v = ((red[0][src] + red[1][src]) + red[2][src]) + red[3][src];
+  const int ch = (isq ? t * 16 : a.Nq + (t - a.Tq) * 16) + em;  // channel in [qkvz | ba] order
+  if (en < a.R && (isq || ch < a.Nq + a.Nb))
+    st_agent(&a.part[((size_t)en * (a.Nq + a.Nb) + ch) * a.SP + s], v);
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) add_agent(sy(a, isq ? sy_group(t * 16 / a.GW) : kSyBa), 1u);
+}
+
+// bf16 weight operand of K step j (32 wide) for this lane: 8 bf16 of row (lane % 16) at
+// k = 32 j + 8 (lane / 16)
 template <bool PACKED>
 __device__ __forceinline__ const u32x4_t* wptr(const Args& a, int t, int j, int lane) {
-  if (PACKED)  // tile t's steps are consecutive 1 KiB blocks, in lane order
-    return reinterpret_cast<const u32x4_t*>(a.wpk + (((size_t)t * a.steps + j) * 64 + lane) * 8);
   const bool isq = t < a.Tq;
+  if (PACKED)  // a tile's steps are consecutive 1 KiB blocks, in lane order
+    return reinterpret_cast<const u32x4_t*>(
+        (isq ? a.wpk + (size_t)t * a.steps * 512 : a.wpk_ba + (size_t)(t - a.Tq) * a.steps * 512) +
+        ((size_t)j * 64 + lane) * 8);
   const int N = isq ? a.Nq : a.Nb;
   // rows past the end are clamped to valid memory; their outputs are never stored
   const int row = min((isq ? t : t - a.Tq) * 16 + (lane & 15), N - 1);
   return reinterpret_cast<const u32x4_t*>((isq ? a.wq : a.wb) + (size_t)row * a.H + 32 * j + 8 * (lane >> 4));
 }
 
+// one split (s of S, nsteps K steps per wave) of a bf16 tile
 template <bool PACKED>
-__device__ void proj_role(const Args& a, int gb, float (*red)[256]) {
-  const int t = gb / a.S, s = gb - t * a.S;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
-  const bool isq = t < a.Tq;
-  const int nsteps = a.spw;
+__device__ void proj_bf16(const Args& a, int gb, int t, int s, int S, int nsteps, float (*red)[256]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // K step of iteration i: the workgroup's 4 waves read 4 adjacent steps at every i. Each
   // workgroup starts at its own point of its K range (a function of the tile and split
   // only), so that the workgroups streaming at the same moment spread over the HBM
@@ -331,8 +412,7 @@ __device__ void proj_role(const Args& a, int gb, float (*red)[256]) {
   for (int u = 0; u < kWin; ++u)
     if (u < nsteps) w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, step_of(u), lane));
 
-  const int copy = gb % kNormCopies;
-  wait_count(sy(a, kSyNorm + copy), (uint32_t)a.R, sy(a, kSyError), kErrNormWait);
+  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)a.R, sy(a, kSyError), kErrNormWait);
   TRACE_POINT(1);
 
   const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
@@ -357,22 +437,118 @@ __device__ void proj_role(const Args& a, int gb, float (*red)[256]) {
     }
   }
   TRACE_POINT(2);
-
-  // D layout: lane l holds channels 4 * (l / 16) + i (i = 0..3) of decode row l % 16
-#pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave][i * 64 + lane] = acc[i];
-  __syncthreads();
-  const int en = tid >> 4, em = tid & 15;  // this thread's (decode row, channel) of the tile
-  const int src = (em & 3) * 64 + (em >> 2) * 16 + en;
-  const float v = ((red[0][src] + red[1][src]) + red[2][src]) + red[3][src];
-  const int ch = (isq ? t * 16 : a.Nq + (t - a.Tq) * 16) + em;  // channel in [qkvz | ba] order
-  if (en < a.R && (isq || ch < a.Nq + a.Nb))
-    st_agent(&a.part[((size_t)en * (a.Nq + a.Nb) + ch) * a.SP + s], v);
-  wait_stores();
-  __syncthreads();
-  if (tid == 0) add_agent(sy(a, isq ? sy_group(t * 16 / a.GW) : kSyBa), 1u);
+  publish_tile(a, t, s, acc, red);
   TRACE_POINT(3);
   TRACE_HWID(7);
+}
+
+// MXFP4 tiles work in units of 4 K steps of 128 (512 K): one weight-scale dword and one
+// activation-scale dword per lane cover a unit, byte `st` serving step st of the unit.
+constexpr int kWinMx = 2;  // units each wave keeps in flight (4 KiB of codes per unit)
+
+struct MxUnit {
+  u32x4_t c[4];  // codes of the unit's 4 steps: 32 e2m1 values of this lane's row and K quarter
+  uint32_t sc;   // the 4 steps' scales of this lane's row and K quarter
+};
+
+template <bool PACKED>
+__device__ __forceinline__ void mx_wload(const Args& a, int t, int U, int lane, MxUnit& m) {
+  const int kb = lane >> 4;
+  if (PACKED) {
+    const u32x4_t* c = reinterpret_cast<const u32x4_t*>(
+        reinterpret_cast<const uint8_t*>(a.wpk) + (((size_t)t * (a.steps >> 2) + 4 * U) * 64 + lane) * 16);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) m.c[st] = __builtin_nontemporal_load(c + 64 * st);
+    m.sc = __builtin_nontemporal_load(a.wpk_sc + ((size_t)t * (a.steps >> 4) + U) * 64 + lane);
+  } else {
+    const int row = t * 16 + (lane & 15);
+    const uint8_t* c = a.wqc + (size_t)row * (a.H >> 1) + 256 * U + 16 * kb;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      m.c[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(c + 64 * st));
+    // the unit's 16 scale bytes of this row: byte 4 st + kb is step st, quarter kb
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(a.wqs + (size_t)row * (a.H >> 5) + 16 * U);
+    m.sc = ((q[0] >> (8 * kb)) & 0xffu) | (((q[1] >> (8 * kb)) & 0xffu) << 8) |
+           (((q[2] >> (8 * kb)) & 0xffu) << 16) | (((q[3] >> (8 * kb)) & 0xffu) << 24);
+  }
+}
+
+__device__ __forceinline__ void mx_xload(const Args& a, int xrow, int U, int lane, MxUnit& m) {
+  const int kb = lane >> 4;
+  const uint8_t* c = reinterpret_cast<const uint8_t*>(a.xq) + (size_t)xrow * (a.H >> 1) + 256 * U + 16 * kb;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) m.c[st] = *reinterpret_cast<const u32x4_t*>(c + 64 * st);
+  m.sc = a.xqs[(size_t)xrow * (a.H >> 7) + 4 * U + kb];
+}
+
+template <int ST>
+__device__ __forceinline__ f32x4_t mx_mfma(const MxUnit& w, const MxUnit& x, f32x4_t acc) {
+  const i32x8_t A = {(int)w.c[ST][0], (int)w.c[ST][1], (int)w.c[ST][2], (int)w.c[ST][3], 0, 0, 0, 0};
+  const i32x8_t B = {(int)x.c[ST][0], (int)x.c[ST][1], (int)x.c[ST][2], (int)x.c[ST][3], 0, 0, 0, 0};
+  // formats 4 = e2m1 for both operands; op_sel picks scale byte ST of each scale dword
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 4, ST, (int)w.sc, ST, (int)x.sc);
+}
+
+// one split of an MXFP4 in_proj_qkvz tile: units s * ups .. (s + 1) * ups - 1, wave w taking
+// units w, w + 4, ... of them
+template <bool PACKED>
+__device__ void proj_mx(const Args& a, int gb, int t, int s, float (*red)[256]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nu = a.ups > wave ? (a.ups - wave + 3) >> 2 : 0;
+  const int rot = nu ? (t * 7 + s * 3) % nu : 0;  // spread concurrent streams over the channels
+  auto unit_of = [&](int m) {
+    const int r = m + rot < nu ? m + rot : m + rot - nu;
+    return s * a.ups + wave + 4 * r;
+  };
+  MxUnit w[kWinMx], x[kWinMx];
+#pragma unroll
+  for (int u = 0; u < kWinMx; ++u)
+    if (u < nu) mx_wload<PACKED>(a, t, unit_of(u), lane, w[u]);
+
+  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)a.R, sy(a, kSyError), kErrNormWait);
+  TRACE_POINT(1);
+
+  const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
+#pragma unroll
+  for (int u = 0; u < kWinMx; ++u)
+    if (u < nu) mx_xload(a, xrow, unit_of(u), lane, x[u]);
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int m0 = 0; m0 < nu; m0 += kWinMx) {
+#pragma unroll
+    for (int u = 0; u < kWinMx; ++u) {
+      const int m = m0 + u;
+      if (m < nu) {
+        acc = mx_mfma<0>(w[u], x[u], acc);
+        acc = mx_mfma<1>(w[u], x[u], acc);
+        acc = mx_mfma<2>(w[u], x[u], acc);
+        acc = mx_mfma<3>(w[u], x[u], acc);
+        if (m + kWinMx < nu) {
+          mx_wload<PACKED>(a, t, unit_of(m + kWinMx), lane, w[u]);
+          mx_xload(a, xrow, unit_of(m + kWinMx), lane, x[u]);
+        }
+      }
+    }
+  }
+  TRACE_POINT(2);
+  publish_tile(a, t, s, acc, red);
+  TRACE_POINT(3);
+  TRACE_HWID(7);
+}
+
+// projection workgroup gb: in_proj_qkvz tiles first (S splits each), then the b|a tiles
+// (Sb splits each)
+template <bool PACKED, bool MX>
+__device__ void proj_role(const Args& a, int gb, float (*red)[256]) {
+  if (gb < a.Gq) {
+    const int t = gb / a.S, s = gb - t * a.S;
+    if (MX)
+      proj_mx<PACKED>(a, gb, t, s, red);
+    else
+      proj_bf16<PACKED>(a, gb, t, s, a.S, a.spw, red);
+  } else {
+    const int g = gb - a.Gq, tb = g / a.Sb, s = g - tb * a.Sb;
+    proj_bf16<PACKED>(a, gb, a.Tq + tb, s, a.Sb, a.spwb, red);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -464,11 +640,11 @@ __device__ __forceinline__ Partials proj_load(const Args& a, int n, int ch) {
   return r;
 }
 // ... added in split order and rounded to bf16: the channel's projection output
-__device__ __forceinline__ float proj_sum(const Args& a, const Partials& r) {
+__device__ __forceinline__ float proj_sum(const Partials& r, int splits) {
   float v = 0.0f;
 #pragma unroll
   for (int q = 0; q < kMaxSplits; ++q)
-    if (q < a.S) v += r.p[q >> 2][q & 3];
+    if (q < splits) v += r.p[q >> 2][q & 3];
   return rbf(v);
 }
 
@@ -512,7 +688,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
 
   // every recurrence workgroup waits, pad rows included (see the counter clearing below)
   wait_count(sy(a, sy_group(kap)), (uint32_t)(a.GW / 16 * a.S), sy(a, kSyError), kErrGroupWait);
-  wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.S), sy(a, kSyError), kErrGroupWait);
+  wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.Sb), sy(a, kSyError), kErrGroupWait);
   TRACE_POINT(1);
 
   uint16_t* core = a.core + (size_t)n * a.nv * DV + (size_t)h * DV;
@@ -533,20 +709,20 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
     TRACE_POINT(5);
     float yq = 0.0f, yk = 0.0f;  // this thread's q and k projection outputs (bf16 values)
     if (qk_thread) {
-      yq = proj_sum(a, p0);
-      yk = proj_sum(a, p1);
+      yq = proj_sum(p0, a.S);
+      yk = proj_sum(p1, a.S);
       sh.qs[tid] = conv_out(c0, yq);
       sh.ks[tid] = conv_out(c1, yk);
     } else if (v_thread) {
-      const float yv = proj_sum(a, p0);
+      const float yv = proj_sum(p0, a.S);
       sh.vs[j] = conv_out(c0, yv);
-      sh.zs[j] = proj_sum(a, p1);
+      sh.zs[j] = proj_sum(p1, a.S);
       conv_store(a, slot, c0, yv);
     }
     if (tid == 64) {
-      sh.scal[3] = __builtin_amdgcn_rcpf(1.0f + __expf(-proj_sum(a, pg)));  // beta = sigmoid(b)
+      sh.scal[3] = __builtin_amdgcn_rcpf(1.0f + __expf(-proj_sum(pg, a.Sb)));  // beta = sigmoid(b)
     } else if (tid == 65) {
-      const float x = proj_sum(a, pg) + dtb;
+      const float x = proj_sum(pg, a.Sb) + dtb;
       const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
       sh.scal[2] = __expf(-__expf(alog) * sp);  // exp(g), g = -exp(A_log) softplus(a + dt_bias)
     }
@@ -641,7 +817,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
 
 // ---------------------------------------------------------------------------------------
 
-template <bool PACKED, int DK, typename ST>
+template <bool PACKED, bool MX, int DK, typename ST>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   __shared__ union {
     float red[4][256];
@@ -650,9 +826,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   const int b = blockIdx.x;
   TRACE_POINT(0);
   if (b < a.R) {
-    norm_role(a, b, sh.red[0]);
+    norm_role<MX>(a, b, sh.red[0]);
   } else if (b < a.R + a.G) {
-    proj_role<PACKED>(a, b - a.R, sh.red);
+    proj_role<PACKED, MX>(a, b - a.R, sh.red);
   } else {
     rec_role<DK, ST>(a, b - a.R - a.G, sh.rec);
   }
@@ -671,6 +847,42 @@ __global__ __launch_bounds__(64) void pack_kernel(const uint16_t* __restrict__ w
   *reinterpret_cast<uint4*>(out + (((size_t)t * (H / 32) + j) * 64 + l) * 8) = v;
 }
 
+// tiled copy of MXFP4 in_proj_qkvz codes: block (t, j) = 64 lanes x 16 bytes, lane l holding
+// the 32 codes of row 16 t + l % 16 at k = 128 j + 32 (l / 16)
+__global__ __launch_bounds__(64) void pack_mx_codes_kernel(const uint8_t* __restrict__ wq, uint8_t* __restrict__ out,
+                                                           int H) {
+  const int j = blockIdx.x, t = blockIdx.y, l = threadIdx.x, row = t * 16 + (l & 15);
+  const uint4 v = *reinterpret_cast<const uint4*>(wq + (size_t)row * (H >> 1) + 64 * j + 16 * (l >> 4));
+  *reinterpret_cast<uint4*>(out + (((size_t)t * (H >> 7) + j) * 64 + l) * 16) = v;
+}
+
+// tiled copy of MXFP4 in_proj_qkvz scales: block (t, U) = 64 lanes x 4 bytes, lane l's byte
+// st holding the scale of row 16 t + l % 16, K step 4 U + st, quarter l / 16
+__global__ __launch_bounds__(64) void pack_mx_scales_kernel(const uint8_t* __restrict__ ws, uint32_t* __restrict__ out,
+                                                            int H) {
+  const int U = blockIdx.x, t = blockIdx.y, l = threadIdx.x, row = t * 16 + (l & 15), kb = l >> 4;
+  const uint8_t* src = ws + (size_t)row * (H >> 5) + 16 * U;
+  uint32_t d = 0;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) d |= (uint32_t)src[4 * st + kb] << (8 * st);
+  out[((size_t)t * (H >> 9) + U) * 64 + l] = d;
+}
+
+// rows of bf16 -> MXFP4 codes [rows, cols/2] (low nibble = even element) and e8m0 scales
+// [rows, cols/32], with the quantiser of the decode kernel; one workgroup per row
+__global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __restrict__ x, uint32_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales, int cols) {
+  const int row = blockIdx.x, nchunk = cols >> 3;
+  for (int i = threadIdx.x; i < nchunk; i += kThreads) {
+    // chunks of one 32-block sit on 4 consecutive lanes, which are active together
+    const uint4 q = *reinterpret_cast<const uint4*>(x + (size_t)row * cols + 8 * i);
+    const uint32_t v[4] = {q.x, q.y, q.z, q.w};
+    uint32_t eb;
+    codes[(size_t)row * nchunk + i] = mx_quant8(v, eb);
+    if ((i & 3) == 0) scales[(size_t)row * (cols >> 5) + (i >> 2)] = (uint8_t)eb;
+  }
+}
+
 }  // namespace
 
 // =======================================================================================
@@ -680,8 +892,12 @@ struct gdn_block {
   gdn_block_config cfg;
   int device;
   int nq, nb, cd, tq, tb, t, splits, spw, steps, sync_words;
+  int sb, spwb, ups;  // b|a tile splits and their steps per wave; MXFP4 units per split
+  bool mx;
   void* scratch;
   uint16_t* xn;
+  uint32_t* xq;
+  uint32_t* xqs;
   float* part;
   uint32_t* sync;
   std::string err;
@@ -710,7 +926,8 @@ std::string check_config(const gdn_block_config* c) {
   if (c->max_rows < 1 || c->max_rows > GDN_MAX_ROWS) add("max_rows must be in 1..16");
   if (c->qkvz_format != GDN_FMT_BF16 && c->qkvz_format != GDN_FMT_MXFP4)
     add("qkvz_format must be GDN_FMT_BF16 or GDN_FMT_MXFP4");
-  if (c->qkvz_format == GDN_FMT_MXFP4) add("MXFP4 in_proj_qkvz is not available in this build");
+  if (c->qkvz_format == GDN_FMT_MXFP4 && c->hidden % 512 != 0)
+    add("MXFP4 in_proj_qkvz needs hidden to be a multiple of 512 (got " + std::to_string(c->hidden) + ")");
   if (c->ssm_state_dtype != GDN_STATE_F32 && c->ssm_state_dtype != GDN_STATE_BF16)
     add("ssm_state_dtype must be GDN_STATE_F32 or GDN_STATE_BF16");
   if (c->has_residual != 0 && c->has_residual != 1) add("has_residual must be 0 or 1");
@@ -725,21 +942,29 @@ int fail(gdn_block* b, int code, const std::string& msg) {
   return code;
 }
 
-template <bool PACKED, int DK>
+template <bool PACKED, bool MX, int DK>
 void launch_dk(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
   if (b->cfg.ssm_state_dtype == GDN_STATE_F32)
-    hipLaunchKernelGGL((decode_kernel<PACKED, DK, float>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<PACKED, MX, DK, float>), dim3(grid), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_kernel<PACKED, DK, uint16_t>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<PACKED, MX, DK, uint16_t>), dim3(grid), dim3(kThreads), 0, st, a);
+}
+
+template <bool PACKED, bool MX>
+void launch_fmt(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
+  switch (b->cfg.head_k_dim) {
+    case 32: launch_dk<PACKED, MX, 32>(b, a, grid, st); break;
+    case 64: launch_dk<PACKED, MX, 64>(b, a, grid, st); break;
+    default: launch_dk<PACKED, MX, 128>(b, a, grid, st); break;
+  }
 }
 
 template <bool PACKED>
 void launch(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
-  switch (b->cfg.head_k_dim) {
-    case 32: launch_dk<PACKED, 32>(b, a, grid, st); break;
-    case 64: launch_dk<PACKED, 64>(b, a, grid, st); break;
-    default: launch_dk<PACKED, 128>(b, a, grid, st); break;
-  }
+  if (b->mx)
+    launch_fmt<PACKED, true>(b, a, grid, st);
+  else
+    launch_fmt<PACKED, false>(b, a, grid, st);
 }
 
 }  // namespace
@@ -766,14 +991,28 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   b->tb = (b->nb + 15) / 16;
   b->t = b->tq + b->tb;
   b->steps = H / 32;
+  b->mx = cfg->qkvz_format == GDN_FMT_MXFP4;
   // K splits: at least one projection workgroup per compute unit, each wave keeping a
-  // whole number of 32-wide steps. Fewer, longer-streaming workgroups measured better than
+  // whole number of K steps. Fewer, longer-streaming workgroups measured better than
   // more, shorter ones (late-dispatched workgroups stay behind in the memory queues). The
-  // count depends on the shape only, never on the row count.
-  int S = 1;
-  while (S < 8 && b->t * S < 256 && b->steps % (4 * 2 * S) == 0) S *= 2;
+  // counts depend on the shape only, never on the row count.
+  int S = 1, Sb;
+  if (!b->mx) {
+    while (S < 8 && b->t * S < 256 && b->steps % (4 * 2 * S) == 0) S *= 2;
+    Sb = S;
+  } else {
+    // MXFP4 tiles split by units of 512 K; the bf16 b|a tiles stream 4x the bytes of an
+    // MXFP4 tile per K, so they take up to 4x the splits
+    const int units = H / 512;
+    while (S < 8 && b->tq * S < 256 && units % (2 * S) == 0) S *= 2;
+    Sb = std::min(8, 4 * S);
+    while (Sb > 1 && b->steps % (4 * Sb) != 0) Sb /= 2;
+    b->ups = units / S;
+  }
   b->splits = S;
   b->spw = b->steps / (4 * S);
+  b->sb = Sb;
+  b->spwb = b->steps / (4 * Sb);
   b->sync_words = (kSyGroup0 + nk + cfg->max_rows * nk) * kLine;
 
   const int R = cfg->max_rows;
@@ -784,8 +1023,10 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
     return o;
   };
   const size_t o_xn = take((size_t)R * H * 2);
-  const size_t o_part = take((size_t)(S > 4 ? 8 : 4) * R * (b->nq + b->nb) * 4);
+  const size_t o_part = take((size_t)(std::max(S, Sb) > 4 ? 8 : 4) * R * (b->nq + b->nb) * 4);
   const size_t o_sync = take((size_t)b->sync_words * 4);
+  const size_t o_xq = b->mx ? take((size_t)R * H / 2) : 0;
+  const size_t o_xqs = b->mx ? take((size_t)R * H / 32) : 0;
 
   hipError_t e = hipGetDevice(&b->device);
   if (e == hipSuccess) e = hipMalloc(&b->scratch, off);
@@ -801,27 +1042,53 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   b->xn = reinterpret_cast<uint16_t*>(base + o_xn);
   b->part = reinterpret_cast<float*>(base + o_part);
   b->sync = reinterpret_cast<uint32_t*>(base + o_sync);
+  b->xq = b->mx ? reinterpret_cast<uint32_t*>(base + o_xq) : nullptr;
+  b->xqs = b->mx ? reinterpret_cast<uint32_t*>(base + o_xqs) : nullptr;
   g_create_error.clear();
   *out = b;
   return GDN_OK;
 }
 
+namespace {
+// tiled copy: [in_proj_qkvz tiles | (MXFP4) their scale blocks | in_proj_ba tiles]
+size_t packed_qkvz_bytes(const gdn_block* b) {
+  const size_t H = b->cfg.hidden;
+  return b->mx ? (size_t)b->nq * H / 2 : (size_t)b->tq * 16 * H * 2;
+}
+size_t packed_scale_bytes(const gdn_block* b) { return b->mx ? (size_t)b->nq * b->cfg.hidden / 32 : 0; }
+}  // namespace
+
 extern "C" size_t gdn_block_packed_weight_bytes(gdn_block_t b) {
   if (!b) return 0;
-  return (size_t)b->t * 16 * b->cfg.hidden * 2;
+  return packed_qkvz_bytes(b) + packed_scale_bytes(b) + (size_t)b->tb * 16 * b->cfg.hidden * 2;
 }
 
 extern "C" int gdn_block_pack_weights(gdn_block_t b, const gdn_block_weights* w, void* packed, void* stream) {
   if (!b) return GDN_E_INVALID_ARG;
   if (!w || !w->w_qkvz || !w->w_ba || !packed)
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w, w->w_qkvz, w->w_ba and packed must not be NULL");
-  if (!aligned16(w->w_qkvz) || !aligned16(w->w_ba) || !aligned16(packed))
+  if (b->mx && !w->w_qkvz_scales)
+    return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w->w_qkvz_scales must not be NULL for MXFP4");
+  if (!aligned16(w->w_qkvz) || !aligned16(w->w_ba) || !aligned16(packed) ||
+      (b->mx && !aligned16(w->w_qkvz_scales)))
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: pointers must be 16-byte aligned");
-  if (b->cfg.qkvz_format != GDN_FMT_BF16)
-    return fail(b, GDN_E_UNSUPPORTED, "gdn_block_pack_weights: only bf16 in_proj_qkvz is tiled");
-  hipLaunchKernelGGL(pack_kernel, dim3(b->steps, b->t), dim3(64), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint16_t*>(w->w_qkvz), static_cast<const uint16_t*>(w->w_ba),
-                     static_cast<uint16_t*>(packed), b->cfg.hidden, b->tq, b->nq, b->nb);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int H = b->cfg.hidden;
+  uint8_t* out = static_cast<uint8_t*>(packed);
+  uint16_t* out_ba = reinterpret_cast<uint16_t*>(out + packed_qkvz_bytes(b) + packed_scale_bytes(b));
+  if (!b->mx) {
+    hipLaunchKernelGGL(pack_kernel, dim3(b->steps, b->t), dim3(64), 0, st, static_cast<const uint16_t*>(w->w_qkvz),
+                       static_cast<const uint16_t*>(w->w_ba), reinterpret_cast<uint16_t*>(out), H, b->tq, b->nq, b->nb);
+  } else {
+    const uint8_t* codes = static_cast<const uint8_t*>(w->w_qkvz);
+    hipLaunchKernelGGL(pack_mx_codes_kernel, dim3(H / 128, b->tq), dim3(64), 0, st, codes, out, H);
+    hipLaunchKernelGGL(pack_mx_scales_kernel, dim3(H / 512, b->tq), dim3(64), 0, st,
+                       static_cast<const uint8_t*>(w->w_qkvz_scales),
+                       reinterpret_cast<uint32_t*>(out + packed_qkvz_bytes(b)), H);
+    // the b|a tiles in the bf16 tile layout (pack_kernel with no in_proj_qkvz tiles)
+    hipLaunchKernelGGL(pack_kernel, dim3(b->steps, b->tb), dim3(64), 0, st, static_cast<const uint16_t*>(w->w_ba),
+                       static_cast<const uint16_t*>(w->w_ba), out_ba, H, 0, 0, b->nb);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(b, GDN_E_HIP, std::string("gdn_block_pack_weights: ") + hipGetErrorString(e));
   return GDN_OK;
@@ -838,12 +1105,13 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
                     std::to_string(rows) + ")");
   if (!w) return fail(b, GDN_E_INVALID_ARG, "gdn_block_decode: weights must not be NULL");
   const bool packed = w->w_proj_packed != nullptr;
+  const void* scales = (b->mx && !packed) ? w->w_qkvz_scales : w->norm_w;  // checked only when read
   const void* ptrs[] = {x, residual, conv_state, ssm_state, state_idx, core_out, w->norm_w,
                         packed ? w->w_proj_packed : w->w_qkvz, packed ? w->w_proj_packed : w->w_ba,
-                        w->conv_w, w->A_log, w->dt_bias, w->gated_norm_w};
+                        w->conv_w, w->A_log, w->dt_bias, w->gated_norm_w, scales};
   const char* names[] = {"x", "residual", "conv_state", "ssm_state", "state_idx", "core_out", "norm_w",
                          packed ? "w_proj_packed" : "w_qkvz", packed ? "w_proj_packed" : "w_ba", "conv_w",
-                         "A_log", "dt_bias", "gated_norm_w"};
+                         "A_log", "dt_bias", "gated_norm_w", (b->mx && !packed) ? "w_qkvz_scales" : "norm_w"};
   for (size_t i = 0; i < sizeof(ptrs) / sizeof(ptrs[0]); ++i) {
     if (!ptrs[i]) return fail(b, GDN_E_INVALID_ARG, std::string("gdn_block_decode: ") + names[i] + " is NULL");
     if (!aligned16(ptrs[i]))
@@ -858,6 +1126,14 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   a.wq = static_cast<const uint16_t*>(w->w_qkvz);
   a.wb = static_cast<const uint16_t*>(w->w_ba);
   a.wpk = static_cast<const uint16_t*>(w->w_proj_packed);
+  a.wpk_sc = packed && b->mx ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(w->w_proj_packed) +
+                                                                 packed_qkvz_bytes(b))
+                             : nullptr;
+  a.wpk_ba = packed ? reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(w->w_proj_packed) +
+                                                        packed_qkvz_bytes(b) + packed_scale_bytes(b))
+                    : nullptr;
+  a.wqc = b->mx ? static_cast<const uint8_t*>(w->w_qkvz) : nullptr;
+  a.wqs = b->mx ? static_cast<const uint8_t*>(w->w_qkvz_scales) : nullptr;
   a.conv_w = static_cast<const uint16_t*>(w->conv_w);
   a.conv_state = static_cast<uint16_t*>(conv_state);
   a.ssm = ssm_state;
@@ -867,6 +1143,8 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   a.gnw = static_cast<const uint16_t*>(w->gated_norm_w);
   a.core = static_cast<uint16_t*>(core_out);
   a.xn = b->xn;
+  a.xq = b->xq;
+  a.xqs = b->xqs;
   a.part = b->part;
   a.sync = b->sync;
   a.H = c.hidden;
@@ -878,9 +1156,13 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   a.Nq = b->nq;
   a.Nb = b->nb;
   a.S = b->splits;
-  a.SP = b->splits > 4 ? 8 : 4;
+  a.SP = std::max(b->splits, b->sb) > 4 ? 8 : 4;
   a.spw = b->spw;
-  a.G = b->t * b->splits;
+  a.Sb = b->sb;
+  a.spwb = b->spwb;
+  a.ups = b->ups;
+  a.Gq = b->tq * b->splits;
+  a.G = a.Gq + b->tb * b->sb;
   a.steps = b->steps;
   a.nk = c.num_k_heads;
   a.dk = c.head_k_dim;
@@ -924,6 +1206,33 @@ extern "C" int gdn_block_trace_copy(unsigned long long* host, size_t blocks) {
                              hipMemcpyDeviceToHost) == hipSuccess ? GDN_OK : GDN_E_HIP;
 }
 #endif
+
+extern "C" int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, void* codes, void* scales,
+                                  void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0) {
+    g_create_error = "gdn_mxfp4_quantize: rows must be >= 0 and cols a positive multiple of 32 (got rows " +
+                     std::to_string(rows) + ", cols " + std::to_string(cols) + ")";
+    return GDN_E_INVALID_ARG;
+  }
+  if (!x || !codes || !scales) {
+    g_create_error = "gdn_mxfp4_quantize: x, codes and scales must not be NULL";
+    return GDN_E_INVALID_ARG;
+  }
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(codes) & 3u)) {
+    g_create_error = "gdn_mxfp4_quantize: x must be 16-byte and codes 4-byte aligned";
+    return GDN_E_INVALID_ARG;
+  }
+  if (rows == 0) return GDN_OK;
+  hipLaunchKernelGGL(mx_quant_kernel, dim3(rows), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(x), static_cast<uint32_t*>(codes), static_cast<uint8_t*>(scales),
+                     (int)cols);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_create_error = std::string("gdn_mxfp4_quantize: launch failed: ") + hipGetErrorString(e);
+    return GDN_E_HIP;
+  }
+  return GDN_OK;
+}
 
 extern "C" void gdn_block_destroy(gdn_block_t b) {
   if (!b) return;

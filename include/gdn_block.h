@@ -31,6 +31,7 @@
  *   w_qkvz (BF16)     [Nqkvz, H] bf16, Nqkvz = 2*nk*dk + 2*nv*dv, K contiguous
  *   w_qkvz (MXFP4)    [Nqkvz, H/2] uint8 e2m1 codes, low nibble = even k,
  *   w_qkvz_scales     [Nqkvz, H/32] uint8 e8m0 (2^(byte-127)), MXFP4 only
+ *                     (MXFP4 needs H to be a multiple of 512)
  *                     Output columns are grouped per key head g:
  *                     [q_g (dk) | k_g (dk) | v_g (r*dv) | z_g (r*dv)], r = nv/nk.
  *   w_ba              [2*nv, H] bf16, grouped per key head: [b_g (r) | a_g (r)]
@@ -45,12 +46,21 @@
  *   core_out          [rows, nv*dv] bf16
  *
  * Tiled projection weights (optional, faster): gdn_block_pack_weights writes a copy
- * of [in_proj_qkvz; in_proj_ba] cut into 16-row tiles whose 32-wide K steps are
- * stored as consecutive 1 KiB blocks in the operand order of the bf16 matrix cores,
- * so every load instruction of the projection reads 1 KiB of contiguous memory.
- * Pass it as w_proj_packed; w_qkvz and w_ba are then not read. The copy is made
- * once (like the pages' shuffled weight copies made before graph capture, "SGLang
- * PR #43558", Modifications / Weights) and has the size of the two matrices.
+ * of [in_proj_qkvz; in_proj_ba] cut into 16-row tiles whose K steps are stored as
+ * consecutive 1 KiB blocks in the operand order of the matrix cores, so every load
+ * instruction of the projection reads 1 KiB of contiguous memory: bf16 tiles in
+ * 32-wide steps; MXFP4 code tiles in 128-wide steps, followed by their scales, one
+ * dword per lane per 4 steps. Pass it as w_proj_packed; w_qkvz, w_qkvz_scales and w_ba
+ * are then not read. The copy is made once (like the pages' shuffled weight copies
+ * made before graph capture, "SGLang PR #43558", Modifications / Weights) and has the
+ * size of the matrices it copies.
+ *
+ * MXFP4 activations: with MXFP4 in_proj_qkvz each xn row is quantised inside the
+ * decode, per 32-element block: the scale exponent e is the smallest integer with
+ * max|xn| <= 6 * 2^e (at least -126), each xn / 2^e is rounded to the nearest e2m1
+ * value with ties to the even code, and a zero code carries no sign ("vLLM PR #60833",
+ * Details / MoE: dynamic MXFP4, 1x32 blocks, RCEIL scales). gdn_mxfp4_quantize applies
+ * the same quantiser to caller rows.
  *
  * Errors: every function returns GDN_OK (0) or a negative code; the message
  * is kept per handle (gdn_block_last_error). A failed check enqueues nothing.
@@ -79,7 +89,7 @@ extern "C" {
 #define GDN_MAX_ROWS 16
 
 typedef struct gdn_block_config {
-  int32_t hidden;          /* H; a multiple of 256 */
+  int32_t hidden;          /* H; a multiple of 256 (of 512 with MXFP4), at most 16384 */
   int32_t num_k_heads;     /* nk */
   int32_t head_k_dim;      /* dk: 32, 64 or 128 */
   int32_t num_v_heads;     /* nv; a multiple of nk */
@@ -134,14 +144,22 @@ int gdn_block_decode(gdn_block_t blk, const void* x, void* residual, const gdn_b
                      void* core_out, void* stream);
 
 /* Size in bytes of the tiled projection copy (16-row tiles of [in_proj_qkvz;
- * in_proj_ba], the last tile zero-padded): T * 16 * H * 2 with
- * T = Nqkvz/16 + ceil(2*nv/16). 0 for a NULL handle. */
+ * in_proj_ba], the last b|a tile zero-padded): Nqkvz*H*2 (bf16) or Nqkvz*H/2 +
+ * Nqkvz*H/32 (MXFP4), plus ceil(2*nv/16) * 16 * H * 2. 0 for a NULL handle. */
 size_t gdn_block_packed_weight_bytes(gdn_block_t blk);
 
-/* Enqueue on `stream` the write of the tiled copy of w->w_qkvz and w->w_ba (bf16,
- * row-major) into `packed` (device memory of gdn_block_packed_weight_bytes bytes,
- * 16-byte aligned, caller-owned). Only for GDN_FMT_BF16. */
+/* Enqueue on `stream` the write of the tiled copy of w->w_qkvz (with w->w_qkvz_scales
+ * for MXFP4) and w->w_ba, all row-major as above, into `packed` (device memory of
+ * gdn_block_packed_weight_bytes bytes, 16-byte aligned, caller-owned). */
 int gdn_block_pack_weights(gdn_block_t blk, const gdn_block_weights* w, void* packed, void* stream);
+
+/* Quantise `rows` rows of `cols` bf16 values (x, [rows, cols], device, 16-byte aligned)
+ * to OCP MXFP4 with the decode's activation quantiser (see above): codes [rows, cols/2]
+ * uint8, two per byte, low nibble = even element (device, 4-byte aligned), and scales
+ * [rows, cols/32] uint8 e8m0 = e + 127 (device). cols must be a positive multiple of 32;
+ * rows == 0 enqueues nothing. Asynchronous on `stream`; allocates nothing. Errors are
+ * reported like a failed gdn_block_create (gdn_block_last_error(NULL)). */
+int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, void* codes, void* scales, void* stream);
 
 /* Read and clear the handle's sticky error word (synchronous; not for the hot
  * path). Inside a decode, every wait for another workgroup is bounded; a wait
@@ -155,7 +173,8 @@ int gdn_block_check(gdn_block_t blk, uint32_t* error_word);
 void gdn_block_destroy(gdn_block_t blk);
 
 /* The last error message of a handle, or of this thread's last failed
- * gdn_block_create when blk is NULL. Never NULL; "" when there was none. */
+ * gdn_block_create or gdn_mxfp4_quantize when blk is NULL. Never NULL; "" when there
+ * was none. */
 const char* gdn_block_last_error(gdn_block_t blk);
 
 #ifdef __cplusplus

@@ -63,28 +63,38 @@ def _ulp_bf16(r):
     return np.exp2(np.floor(np.log2(a)) - 7)
 
 
-def close(name, got, ref, bf16=True):
-    """Assert the parity rule; returns (max_abs, count above ABS_TOL)."""
+def close(name, got, ref, bf16=True, flips=None):
+    """Assert the parity rule; returns (max_abs, count above ABS_TOL, count outside the bound).
+
+    `flips` = (fraction, cap) relaxes the element rule for outputs downstream of the
+    MXFP4 activation quantiser: up to `fraction` of the elements may leave the bound, each
+    by at most `cap` (see tests/test_gpu_mxfp4.py for why); the cosine rule still holds."""
     g = og.bf16_to_f64(got) if bf16 else np.asarray(got, np.float64)
     r = og.bf16_to_f64(ref) if bf16 else np.asarray(ref, np.float64)
     g, r = g.reshape(-1), r.reshape(-1)
     if g.size == 0:
-        return 0.0, 0
+        return 0.0, 0, 0
     assert np.all(np.isfinite(g)), f"{name}: non-finite values"
     err = np.abs(g - r)
     bound = np.maximum(ABS_TOL, _ulp_bf16(r)) if bf16 else np.full_like(r, ABS_TOL)
     bad = err > bound
-    assert not bad.any(), (f"{name}: {bad.sum()} of {err.size} outside the bound; worst err "
-                           f"{err.max():.4g} at {np.argmax(err)} (gpu {g[np.argmax(err)]}, oracle {r[np.argmax(err)]})")
+    worst = (f"worst err {err.max():.4g} at {np.argmax(err)} (gpu {g[np.argmax(err)]}, "
+             f"oracle {r[np.argmax(err)]})")
+    if flips is None:
+        assert not bad.any(), f"{name}: {bad.sum()} of {err.size} outside the bound; {worst}"
+    else:
+        frac, cap = flips
+        assert bad.sum() <= frac * err.size, f"{name}: {bad.sum()} of {err.size} outside the bound; {worst}"
+        assert err.max() <= cap, f"{name}: an error above the cap {cap}; {worst}"
     nr, ng = np.linalg.norm(r), np.linalg.norm(g)
     if nr > 0:
         cos = float(g @ r / (nr * ng))
         assert cos >= COS_MIN, f"{name}: cosine {cos}"
-    return float(err.max()), int((err > ABS_TOL).sum())
+    return float(err.max()), int((err > ABS_TOL).sum()), int(bad.sum())
 
 
-def check_parity(shape, w, call, out, label=""):
-    """Compare one GPU decode's outputs with the oracle's."""
+def check_parity(shape, w, call, out, label="", flips=None):
+    """Compare one GPU decode's outputs with the oracle's (`flips`: see close())."""
     ref = run_oracle(shape, w, call)
     idx = call.state_idx.numpy()
     valid = idx > 0
@@ -94,7 +104,7 @@ def check_parity(shape, w, call, out, label=""):
     # pad rows: all +0.0
     assert np.all(core[~valid] == 0), f"{label}: pad row core not +0"
     stats = {}
-    stats["core"] = close(f"{label} core", core[valid], ref["core"][valid])
+    stats["core"] = close(f"{label} core", core[valid], ref["core"][valid], flips=flips)
     slots = idx[valid]
     conv_g, conv_r = u16(out["conv_state"]), ref["conv_state"]
     bf16_state = shape.ssm_state_dtype == "bf16"
@@ -104,6 +114,24 @@ def check_parity(shape, w, call, out, label=""):
     assert np.array_equal(ssm_g[untouched], oracle_state(call.ssm_state)[untouched]), \
         f"{label}: untouched ssm slot changed"
     if len(slots):
-        stats["conv"] = close(f"{label} conv_state", conv_g[slots], conv_r[slots])
-        stats["ssm"] = close(f"{label} ssm_state", ssm_g[slots], ssm_r[slots], bf16=bf16_state)
+        stats["conv"] = close(f"{label} conv_state", conv_g[slots], conv_r[slots], flips=flips)
+        stats["ssm"] = close(f"{label} ssm_state", ssm_g[slots], ssm_r[slots], bf16=bf16_state, flips=flips)
+    return stats
+
+
+def parity_case(shape, rows, seed, *, pads=None, all_pad=False, stress=False, max_rows=None,
+                weights=None, call=None, flips=None, dev="cuda:0"):
+    """One decode of `shape` on seeded inputs (or the given weights / call), with the
+    row-major and the tiled weights (which must agree bit for bit), against the oracle."""
+    from gated_deltanet_linear_decode_amd import synth
+    note(f"case {shape.name} rows={rows} seed={seed} pads={pads} all_pad={all_pad} stress={stress}")
+    w = weights if weights is not None else synth.make_weights(shape, seed, gated_norm_stress=stress)
+    c = call if call is not None else synth.make_call(shape, rows, seed, pads=pads, all_pad=all_pad)
+    blk = GdnBlock(shape, max_rows=max_rows or max(rows, shape.max_rows), device=dev)
+    wd, cd = weights_to(w, dev), call_to(c, dev)
+    out = run_gpu(blk, shape, wd, cd)
+    same_bits(out, run_gpu(blk, shape, wd, cd, packed=blk.pack(wd)))
+    blk.close()
+    stats = check_parity(shape, w, c, out, label=f"{shape.name}/r{rows}/s{seed}", flips=flips)
+    note(f"  ok {stats}")
     return stats

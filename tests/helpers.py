@@ -41,3 +41,37 @@ def run_oracle(shape, weights, call):
     return oracle.decode_block(oracle_cfg(shape), oracle_weights(weights), u16(call.x),
                                u16(call.residual), u16(call.conv_state),
                                oracle_state(call.ssm_state), call.state_idx.numpy().copy())
+
+
+def pow2_rows(hidden: int, rows: int, seed: int):
+    """Rows whose Gemma RMSNorm (weight 0) is exact on any hardware, and the exact norm.
+
+    Every element is 0 or +-2^p (p in -4..1); the last 64 elements fill the row's sum of
+    squares up to hidden * 4^j for the smallest such j (base-4 digits of the remainder),
+    so mean(h^2) = 4^j exactly, rstd = 2^-j (1 - delta) with delta <= 5e-7 for eps = 1e-6,
+    and bf16(h * rstd) = h * 2^-j exactly: far from any bf16 rounding boundary. Sums of
+    these squares are exact in f32 up to hidden = 8192. Returns (x [rows, H] float64,
+    xn [rows, H] float64)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    body = hidden - 64
+    x = np.zeros((rows, hidden))
+    xn = np.zeros((rows, hidden))
+    for r in range(rows):
+        p = rng.integers(-4, 2, size=body)
+        v = np.where(rng.random(body) < 0.1, 0.0, rng.choice([-1.0, 1.0], size=body) * np.exp2(p))
+        ss = float(np.sum(v * v))
+        j = 0
+        while hidden * 4.0 ** j < ss:
+            j += 1
+        rem = int(round((hidden * 4.0 ** j - ss) * 256))  # 256 * (sum the filler must add)
+        fill, m = [], 0
+        while rem:
+            fill += [2.0 ** (m - 4)] * (rem % 4)  # (2^(m-4))^2 = 4^m / 256
+            rem //= 4
+            m += 1
+        assert len(fill) <= 64
+        fill = np.array(fill + [0.0] * (64 - len(fill))) * rng.choice([-1.0, 1.0], size=64)
+        x[r] = np.concatenate([v, fill])
+        assert float(np.sum(x[r] * x[r])) == hidden * 4.0 ** j
+        xn[r] = x[r] * 2.0 ** -j
+    return x, xn

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "gdn_block.h")
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_block_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -74,6 +74,28 @@ def test_create_lists_every_reason():
     msg = str(e.value)
     for needle in ("hidden", "conv_width", "max_rows", "has_residual"):
         assert needle in msg
+
+
+def test_mxfp4_needs_hidden_multiple_of_512():
+    with pytest.raises(abi.GdnError) as e:
+        abi.gdn_block_create(_cfg(qkvz_format=abi.GDN_FMT_MXFP4))  # the tiny shape has H = 256
+    assert e.value.code == abi.GDN_E_UNSUPPORTED and "512" in str(e.value)
+
+
+def test_quantize_arguments_are_checked_on_the_host():
+    lib = abi.load()
+    fake = 1 << 20  # an aligned address that is never dereferenced: every call below is refused
+    for rows, cols, x, codes, scales, needle in [
+        (1, 48, fake, fake, fake, "multiple of 32"),
+        (-1, 32, fake, fake, fake, "rows"),
+        (1, 0, fake, fake, fake, "cols"),
+        (1, 32, None, fake, fake, "NULL"),
+        (1, 32, fake + 8, fake, fake, "aligned"),
+        (1, 32, fake, fake + 2, fake, "aligned"),
+    ]:
+        assert lib.gdn_mxfp4_quantize(x, rows, cols, codes, scales, None) == abi.GDN_E_INVALID_ARG
+        assert needle in abi.gdn_block_last_error(None)
+    assert lib.gdn_mxfp4_quantize(fake, 0, 32, fake, fake, None) == abi.GDN_OK  # nothing to do
 
 
 def test_null_arguments_are_rejected_on_the_host():

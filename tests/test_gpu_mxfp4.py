@@ -1,0 +1,142 @@
+"""GPU parity of the MXFP4 in_proj_qkvz path ("vLLM PR #60833", Details / MoE and MXFP4
+layouts: MXFP4 weights with dynamic MXFP4 activations in 1x32 blocks, RCEIL scales).
+
+Three kinds of checks:
+
+* the activation quantiser alone (gdn_mxfp4_quantize, the device function the decode
+  uses) against the oracle's, bit for bit, on the same bf16 input, including ties,
+  the scale-exponent boundaries, zero and subnormal blocks and random bit patterns;
+* whole decodes on rows whose norm is exact on both sides (tests.helpers.pow2_rows), so
+  GPU and oracle quantise the same xn: the usual element rule applies unchanged;
+* whole decodes on the workloads' N(0, 1) rows. There the kernel's f32 rstd can leave
+  an xn element one bf16 ulp away from the oracle's f64 result (about one element in
+  16000), and when that element sits next to an e2m1 rounding boundary its code moves
+  by one step. Every output of that row then moves by |w| * step * 2^e: with weights
+  of at most 6 * 2^-7 and activation steps of at most 1 at these magnitudes, 0.05 per
+  flip. Such rows may leave the 2e-2 element bound, so these cases allow up to 2 % of
+  the elements outside it, none by more than 0.15 (three flips on one row), and keep
+  the cosine >= 0.9999 rule. The counts are printed for every case.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_linear_decode_amd import abi, configs, synth
+from oracle import gdn as og
+from tests.gpu_util import note, parity_case
+from tests.helpers import from_u16, pow2_rows, u16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+FLIPS = (0.02, 0.15)
+
+TINY_MX = configs.GdnShape(
+    "tiny_mxfp4", hidden=512, num_k_heads=2, head_k_dim=32, num_v_heads=4, head_v_dim=32,
+    num_state_slots=24, ssm_state_dtype="f32", has_residual=True, qkvz_format="mxfp4",
+    rows=(16,), pad_rows=True)
+
+
+def _quantizer_inputs(cols, seed):
+    """bf16 bit patterns [7, cols] covering the quantiser's cases."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nb = cols // 32
+    rows = []
+    rows.append(og.f64_to_bf16(rng.normal(0, 1, cols)))
+    scale = np.repeat(np.exp2(rng.integers(-130, 120, nb).astype(np.float64)), 32)
+    rows.append(og.f64_to_bf16(rng.normal(0, 1, cols) * scale))
+    # ties and grid points, each block anchored at 6 * 2^e
+    vals = np.array([0, .25, .5, .75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6])
+    t = rng.choice(vals, size=(nb, 32)) * rng.choice([-1.0, 1.0], size=(nb, 32))
+    t[:, 0] = 6.0
+    e = rng.integers(-120, 120, nb).astype(np.float64)
+    rows.append(og.f64_to_bf16((t * np.exp2(e)[:, None]).reshape(-1)))
+    # zero blocks, negative zeros, maxima at and just above 1.5 * 2^E
+    z = rng.normal(0, 1, (nb, 32))
+    z[0::4] = 0.0
+    z[1::4] = -0.0
+    z[2::4, 0] = 1.5 * 2.0 ** rng.integers(-20, 20)
+    z[2::4, 1:] = np.clip(z[2::4, 1:], -1.4, 1.4) * np.abs(z[2::4, :1])
+    zb = og.f64_to_bf16(z.reshape(-1)).reshape(nb, 32)
+    zb[3::4, 0] = og.f64_to_bf16(np.array([1.5 * 2.0 ** 3]))[0] + 1  # 1.5 * 2^3 plus one ulp
+    rows.append(zb.reshape(-1))
+    # subnormal and tiny normal values: the scale exponent clamps at -126
+    sub = rng.integers(1, 128, cols).astype(np.uint16) | (rng.integers(0, 2, cols).astype(np.uint16) << 15)
+    tiny = og.f64_to_bf16(rng.normal(0, 1, cols) * 2.0 ** -125)
+    rows.append(np.where(rng.random(cols) < 0.5, sub, tiny).astype(np.uint16))
+    # random finite bit patterns
+    bits = rng.integers(0, 1 << 16, cols).astype(np.uint16)
+    bits = np.where((bits & 0x7F80) == 0x7F80, bits & 0xBFFF, bits).astype(np.uint16)
+    rows.append(bits)
+    # values one bf16 ulp either side of the rounding boundaries
+    b = np.array([.25, .75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    bb = og.f64_to_bf16(rng.choice(b, size=(nb, 32)) * 2.0)  # block scale 2^1 after the anchor
+    bb = (bb.astype(np.int32) + rng.integers(-1, 2, size=(nb, 32))).astype(np.uint16)
+    bb[:, 0] = og.f64_to_bf16(np.array([12.0]))[0]
+    rows.append(bb.reshape(-1))
+    return np.stack(rows).astype(np.uint16)
+
+
+@pytest.mark.parametrize("cols", [32, 1120, 8192])
+def test_quantizer_bit_exact(cols):
+    """Codes and scales equal the oracle's for every element ("vLLM PR #60833", Details:
+    RCEIL scales; ties to the even code)."""
+    x = _quantizer_inputs(cols, 40 + cols)
+    R = x.shape[0]
+    note(f"quantiser rows={R} cols={cols}")
+    xd = from_u16(x).to(DEV)
+    codes = torch.zeros(R, cols // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.zeros(R, cols // 32, dtype=torch.uint8, device=DEV)
+    abi.gdn_mxfp4_quantize(xd.data_ptr(), R, cols, codes.data_ptr(), scales.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = og.mxfp4_quantize(og.bf16_to_f64(x))
+    packed = (ref_codes[:, 0::2] | (ref_codes[:, 1::2] << 4)).astype(np.uint8)
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(got_s, ref_scales), np.argwhere(got_s != ref_scales)[:5]
+    bad = np.argwhere(got_c != packed)
+    assert bad.size == 0, f"{len(bad)} code bytes differ, first at {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("rows", [1, 4, 7, 16])
+@pytest.mark.parametrize("state", ["f32", "bf16"])
+def test_tiny_mxfp4(rows, state):
+    parity_case(TINY_MX.with_(ssm_state_dtype=state), rows, 200 + rows, flips=FLIPS, dev=DEV)
+
+
+@pytest.mark.parametrize("hidden,dk", [(1536, 32), (2048, 128), (4096, 64)])
+def test_mxfp4_shapes(hidden, dk):
+    """Hidden sizes with 3, 4 and 8 units of 512 K per tile (idle waves when a split has
+    fewer than 4 units), and every head size."""
+    shape = TINY_MX.with_(name=f"mx_h{hidden}_d{dk}", hidden=hidden, head_k_dim=dk, head_v_dim=dk,
+                          num_v_heads=6)
+    parity_case(shape, 8, 300 + dk, flips=FLIPS, dev=DEV)
+
+
+@pytest.mark.parametrize("rows", [1, 5, 8, 13, 16])
+def test_tp8_rank_mxfp4(rows):
+    parity_case(configs.TP8_RANK_MXFP4, rows, 31, flips=FLIPS, dev=DEV)
+
+
+def test_tp8_rank_mxfp4_all_pad():
+    parity_case(configs.TP8_RANK_MXFP4, 3, 32, all_pad=True, dev=DEV)
+
+
+def _exact_case(shape, rows, seed):
+    shape = shape.with_(has_residual=False)
+    w = synth.make_weights(shape, seed)
+    w.norm_w = torch.zeros_like(w.norm_w)
+    c = synth.make_call(shape, rows, seed)
+    x, _ = pow2_rows(shape.hidden, rows, seed)
+    c.x = from_u16(og.f64_to_bf16(x))
+    return parity_case(shape, rows, seed, weights=w, call=c, dev=DEV)
+
+
+@pytest.mark.parametrize("rows", [1, 16])
+def test_exact_activations_tiny(rows):
+    """Rows with an exact norm: the strict element rule on every output."""
+    _exact_case(TINY_MX, rows, 60 + rows)
+
+
+@pytest.mark.parametrize("rows", [3, 16])
+def test_exact_activations_tp8_rank(rows):
+    _exact_case(configs.TP8_RANK_MXFP4, rows, 70 + rows)

@@ -4,27 +4,15 @@ the full sizes of each workload (all rows, pad rows, all-pad calls)."""
 import pytest
 import torch
 
-from gated_deltanet_linear_decode_amd import configs, synth
-from gated_deltanet_linear_decode_amd.block import GdnBlock
-from tests.gpu_util import call_to, check_parity, note, run_gpu, same_bits, weights_to
+from gated_deltanet_linear_decode_amd import configs
+from tests.gpu_util import parity_case
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _case(shape, rows, seed, *, pads=None, all_pad=False, stress=False, max_rows=None):
-    note(f"case {shape.name} rows={rows} seed={seed} pads={pads} all_pad={all_pad} stress={stress}")
-    w = synth.make_weights(shape, seed, gated_norm_stress=stress)
-    call = synth.make_call(shape, rows, seed, pads=pads, all_pad=all_pad)
-    blk = GdnBlock(shape, max_rows=max_rows or max(rows, shape.max_rows), device=DEV)
-    wd, cd = weights_to(w, DEV), call_to(call, DEV)
-    out = run_gpu(blk, shape, wd, cd)
-    # the tiled weight copy gives the same bits as the row-major weights
-    same_bits(out, run_gpu(blk, shape, wd, cd, packed=blk.pack(wd)))
-    blk.close()
-    stats = check_parity(shape, w, call, out, label=f"{shape.name}/r{rows}/s{seed}")
-    note(f"  ok {stats}")
-    return stats
+def _case(shape, rows, seed, **kw):
+    return parity_case(shape, rows, seed, dev=DEV, **kw)
 
 
 @pytest.mark.parametrize("seed", range(8))

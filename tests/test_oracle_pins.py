@@ -386,3 +386,22 @@ def test_gated_norm_constant_head_and_zero_gate():
     assert np.array_equal(got, expect)
     zero = og.gated_rmsnorm(_bf(np.linspace(-1, 1, 32)), _bf(np.zeros(32)), w, 1e-6)
     assert np.all(og.bf16_to_f64(zero) == 0.0)
+
+
+def test_pow2_rows_have_an_exact_norm():
+    """The exact-activation rows of the MXFP4 GPU tests: the oracle's norm (weight 0,
+    eps 1e-6) returns h * 2^-j bit for bit, and its MXFP4 image is the exact one."""
+    from tests.helpers import pow2_rows
+    for hidden in (512, 8192):
+        x, xn_exact = pow2_rows(hidden, 3, 5)
+        bits = og.f64_to_bf16(x)
+        assert np.array_equal(og.bf16_to_f64(bits), x)  # representable in bf16
+        xn = og.gemma_rmsnorm(bits, og.f64_to_bf16(np.zeros(hidden)), 1e-6)
+        assert np.array_equal(og.bf16_to_f64(xn), xn_exact)
+        codes, scales = og.mxfp4_quantize(xn_exact)
+        # powers of two at most 4 steps below the block maximum are exact in e2m1 (0.25 x
+        # the maximum's code value rounds to 0 as a tie to even)
+        deq = og.mxfp4_dequantize(codes, scales)
+        blocks = np.abs(xn_exact).reshape(3, -1, 32).max(axis=-1)
+        small = np.abs(xn_exact) < np.repeat(blocks, 32, axis=-1) / 8
+        assert np.array_equal(deq[~small], xn_exact[~small])
