@@ -45,7 +45,7 @@ def log(msg):
 class Rotation:
     """`layers` copies of one layer's weights and state pools on the device."""
 
-    def __init__(self, shape, layers, max_rows, seed=0):
+    def __init__(self, shape, layers, max_rows, seed=0, pads=False):
         import torch
 
         from gated_deltanet_linear_decode_amd import synth
@@ -55,7 +55,7 @@ class Rotation:
         self.shape, self.dev = shape, dev
         self.blk = GdnBlock(shape, max_rows=max_rows, device=dev)
         self.w_cpu = synth.make_weights(shape, seed)
-        self.call_cpu = synth.make_call(shape, max_rows, seed, pads=False)
+        self.call_cpu = synth.make_call(shape, max_rows, seed, pads=pads)
         self.copies = []
         for i in range(layers):
             w = synth.GdnWeights(**{k: (v.to(dev).clone() if v is not None else None)
@@ -116,6 +116,36 @@ class Rotation:
         return start.elapsed_time(end) * 1000.0 / steps
 
 
+    def valid_rows(self, rows):
+        return int((self.call_cpu.state_idx[:rows] > 0).sum())
+
+    def close(self):
+        import torch
+        self.copies.clear()
+        self.blk.close()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def sweep_workload(shape, rows_list, steps, packed=True):
+    """µs per launch of `shape` (its own layer count, pad rows as the workload has them)."""
+    rot = Rotation(shape, shape.layers, max(rows_list), pads=shape.pad_rows)
+    out = {}
+    for r in rows_list:
+        t = rot.time(r, steps, steps // 4, packed=packed)
+        b = configs_mod().algorithmic_bytes(shape, r, rot.valid_rows(r))
+        out[str(r)] = dict(us=round(t, 3), valid_rows=rot.valid_rows(r), algo_bytes=b,
+                           gbs=round(b / (t * 1e-6) / 1e9, 1), frac=round(b / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+        log(f"{shape.name} rows {r}: {t:.2f} us/launch")
+    rot.close()
+    return out
+
+
+def configs_mod():
+    from gated_deltanet_linear_decode_amd import configs
+    return configs
+
+
 def cpu_baseline(shape, rot, rows, seconds):
     """The oracle on the same workload (same bytes), timed for about `seconds`."""
     import numpy as np
@@ -164,6 +194,8 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=960)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workloads", default="tp8_rank_f32_state_pads,dense_full_width,tp8_rank_mxfp4",
+                    help="other workloads to sweep (tiled weights) after the headline; '' for none")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -206,6 +238,14 @@ def main():
                                       frac=round(b / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
             log(f"rows {r} {key}: {t:.2f} us/launch")
 
+    workloads = {}
+    for name in [n for n in args.workloads.split(",") if n]:
+        wl = configs.ALL[name]
+        rows_list = [r for r in (1, 2, 4, 8, 12, 16) if r <= wl.max_rows] if wl.max_rows >= 8 else list(wl.rows)
+        rows_list = sorted(set(rows_list) | set(wl.rows) if len(wl.rows) <= 8 else rows_list)
+        log(f"sweeping {name}: rows {rows_list}, {wl.layers} layer copies")
+        workloads[name] = sweep_workload(wl, rows_list, args.sweep_steps)
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -246,6 +286,7 @@ def main():
             "algo_bytes_per_launch": algo, "kernel": "decode_kernel (the whole block, one launch)",
         },
         "sweep": sweep,
+        "workloads": workloads,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

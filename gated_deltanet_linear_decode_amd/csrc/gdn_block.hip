@@ -5,14 +5,17 @@
 // (the front of a GDN layer as one launch, "sgl-amd-mono PR #89", Modifications; the
 // "GDN block" of "vLLM PR #60833", Details / Launches):
 //
-//   [0, R)            norm: one workgroup per row. h = bf16(x + residual),
-//                     xn = bf16(h * rstd * (1 + w)) published to scratch, then the row is
-//                     counted done and the residual row is rewritten with h. No workgroup
+//   [0, R*P)          norm: P = ceil(H / 2048) workgroups per row. Each loads the whole row,
+//                     forms h = bf16(x + residual) and the row's rstd (all P in the same
+//                     order, so with the same result), and publishes one 2048-wide slice of
+//                     xn = bf16(h * rstd * (1 + w)) to scratch; then it counts itself done
+//                     and rewrites its slice of the residual row with h (with a residual
+//                     input, once every norm workgroup has loaded its row). No workgroup
 //                     holds x in LDS; every projection workgroup reads the finished xn
 //                     ("vLLM PR #60833", Details / x without an LDS tile).
-//                     With MXFP4 in_proj_qkvz the row is also quantised to MXFP4 (codes +
+//                     With MXFP4 in_proj_qkvz the slice is also quantised to MXFP4 (codes +
 //                     one e8m0 scale per 32) into a second scratch image.
-//   [R, R+G)          projection: in_proj_qkvz and in_proj_ba as one skinny GEMM on the
+//   [R*P, R*P+G)      projection: in_proj_qkvz and in_proj_ba as one skinny GEMM on the
 //                     matrix cores: bf16 weights on v_mfma_f32_16x16x32_bf16, MXFP4 weights
 //                     on v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 x fp4 with per-32 scales);
 //                     16 weight rows x 16 decode rows per instruction. Each workgroup owns
@@ -20,7 +23,7 @@
 //                     first, then waits for the norm rows, multiplies, and publishes its f32
 //                     partial sums; then it counts itself done for the tile's key-head group
 //                     (or for the b|a tiles).
-//   [R+G, R+G+R*nv)   recurrence: one workgroup per (row, value head). It loads its
+//   [R*P+G, +R*nv)    recurrence: one workgroup per (row, value head). It loads its
 //                     dk x dv state tile and its conv state and taps first, waits for its
 //                     key-head group and the b|a tiles, adds the split partials of its
 //                     channels in split order and rounds them to bf16 (the projection
@@ -29,9 +32,11 @@
 //                     The q|k conv state of a key head is shared by its r value heads: the
 //                     last of them writes it once the others have read the old rows.
 //
-// Waits only ever target workgroups with lower block ids, which the dispatcher starts
-// first, so every wait ends; each is also bounded and records a sticky error word if it
-// gives up. Data handed from one workgroup to another travels as agent-scope atomic
+// Every wait ends: projection and recurrence workgroups wait only for workgroups with
+// lower block ids, which the dispatcher starts first, and a norm workgroup's one wait
+// (before its residual rewrite) is for the other norm workgroups, which count themselves
+// before they wait for anything. Each wait is also bounded and records a sticky error
+// word if it gives up. Data handed from one workgroup to another travels as agent-scope atomic
 // stores (coherent across the XCDs' L2s, one access at a time) followed by a wait for
 // the stores; readers poll counters with agent-scope atomic loads. No device-wide fence
 // is used: on gfx950 one writes back and invalidates a whole L2. Every counter is
@@ -179,11 +184,11 @@ __device__ unsigned long long g_trace[kTraceBlocks * kTraceSlots];
   } while (0)
 #endif
 
-// sync word lines (one 128-byte line each): norm rows done (kNormCopies copies, polled
-// spread out); b|a tile splits done; recurrence workgroups finished; the sticky error
-// word; then per key-head group: tile splits done; then per (row, key-head group): value
-// heads that have read the old q|k conv rows.
-enum { kSyNorm = 0, kSyBa = kNormCopies, kSyExit, kSyError, kSyGroup0 };
+// sync word lines (one 128-byte line each): norm workgroups done (kNormCopies copies,
+// polled spread out); b|a tile splits done; recurrence workgroups finished; the sticky
+// error word; norm workgroups finished; then per key-head group: tile splits done; then
+// per (row, key-head group): value heads that have read the old q|k conv rows.
+enum { kSyNorm = 0, kSyBa = kNormCopies, kSyExit, kSyError, kSyNormExit, kSyGroup0 };
 enum : uint32_t { kErrNormWait = 1u, kErrGroupWait = 2u, kErrConvWait = 4u };
 
 // ---------------------------------------------------------------------------------------
@@ -212,12 +217,13 @@ struct Args {
   uint16_t* xn;              // [R, H]
   uint32_t* xq;              // MXFP4 image of xn: codes [R, H/2] bytes
   uint32_t* xqs;             // MXFP4 image of xn: scales [R, H/32] bytes, grouped per 4 K steps
-  float* part;               // [R, Nq + Nb, SP] split partials of the projections (SP = S rounded up to 4)
+  float* part;               // [S, R, Nq + Nb] split partials of the projections
   uint32_t* sync;            // sync word lines
   // sizes
-  int H, R, has_res;
-  int T, Tq, Tb, Nq, Nb, S, SP, spw, G, steps;  // tiles, splits, padded splits, K steps per wave, projection WGs
-  int Sb, spwb, Gq, ups;     // b|a tile splits and steps per wave; qkvz workgroups; MXFP4 units per split
+  int H, R, has_res, P;  // P: norm workgroups per row
+  int T, Tq, Tb, Nq, Nb, steps;  // tiles (all, in_proj_qkvz, in_proj_ba), channels, 32-wide K steps of H
+  int S, Kr, G, Gq;              // K ranges (splits) of Kr each, projection workgroups, of which
+                                 // in_proj_qkvz ones
   int nk, dk, nv, dv, r, GW, Cd, slots;
   float eps, l2eps, geps;
 };
@@ -265,45 +271,50 @@ __device__ __forceinline__ uint32_t mx_quant8(const uint32_t* v, uint32_t& ebyte
 }
 
 template <bool MX>
-__device__ void norm_role(const Args& a, int row, float* red) {
-  const int H = a.H, nchunk = H >> 3;
+__device__ void norm_role(const Args& a, int b, float* red) {
+  // P workgroups per row: each loads and sums the whole row (the same sum in the same
+  // order, so the same rstd in all of them) and produces xn for one slice of 256 chunks
+  // of 8 elements, so no thread converts more than one chunk
+  const int row = b / a.P, part = b - row * a.P;
+  const int H = a.H, nchunk = H >> 3, tid = threadIdx.x;
   const uint4* xp = reinterpret_cast<const uint4*>(a.x + (size_t)row * H);
   uint4* rp = reinterpret_cast<uint4*>(a.residual + (size_t)row * H);
-  const uint4* wp = reinterpret_cast<const uint4*>(a.norm_w);
-  uint4 hv[kNormMaxChunks], wv[kNormMaxChunks];
+  const int mi = part * kThreads + tid;  // this thread's chunk of the slice
+  uint4 hv[kNormMaxChunks], rv[kNormMaxChunks], wv = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int c = 0; c < kNormMaxChunks; ++c) {  // every load of the row is issued up front
-    const int i = threadIdx.x + c * kThreads;
-    if (i < nchunk) hv[c] = xp[i], wv[c] = wp[i];
+    const int i = tid + c * kThreads;
+    if (i < nchunk) hv[c] = xp[i];
   }
-  uint4 rv[kNormMaxChunks];
   if (a.has_res) {
 #pragma unroll
     for (int c = 0; c < kNormMaxChunks; ++c) {
-      const int i = threadIdx.x + c * kThreads;
+      const int i = tid + c * kThreads;
       if (i < nchunk) rv[c] = rp[i];
     }
   }
+  if (mi < nchunk) wv = reinterpret_cast<const uint4*>(a.norm_w)[mi];
   float ss = 0.0f;
+  uint4 mine = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int c = 0; c < kNormMaxChunks; ++c) {
-    const int i = threadIdx.x + c * kThreads;
+    const int i = tid + c * kThreads;
     if (i < nchunk) {
       uint4 v = hv[c];
       if (a.has_res) {
-        const uint4 b = rv[c];
+        const uint4 q = rv[c];
         uint32_t* pv = reinterpret_cast<uint32_t*>(&v);
-        const uint32_t* pb = reinterpret_cast<const uint32_t*>(&b);
+        const uint32_t* pb = reinterpret_cast<const uint32_t*>(&q);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          pv[q] = f2bf2(bf2f((uint16_t)pv[q]) + bf2f((uint16_t)pb[q]),
-                        bf2f((uint16_t)(pv[q] >> 16)) + bf2f((uint16_t)(pb[q] >> 16)));
+        for (int k = 0; k < 4; ++k)
+          pv[k] = f2bf2(bf2f((uint16_t)pv[k]) + bf2f((uint16_t)pb[k]),
+                        bf2f((uint16_t)(pv[k] >> 16)) + bf2f((uint16_t)(pb[k] >> 16)));
       }
-      hv[c] = v;
+      if (c == part) mine = v;
       const uint32_t* ph = reinterpret_cast<const uint32_t*>(&v);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float l = bf2f((uint16_t)ph[q]), h = bf2f((uint16_t)(ph[q] >> 16));
+      for (int k = 0; k < 4; ++k) {
+        const float l = bf2f((uint16_t)ph[k]), h = bf2f((uint16_t)(ph[k] >> 16));
         ss = fmaf(l, l, ss);
         ss = fmaf(h, h, ss);
       }
@@ -312,55 +323,66 @@ __device__ void norm_role(const Args& a, int row, float* red) {
   ss = block_sum(ss, red);
   TRACE_POINT(1);
   const float rstd = 1.0f / sqrtf(ss / (float)H + a.eps);
-  uint32_t* op = reinterpret_cast<uint32_t*>(a.xn + (size_t)row * H);
+  if (mi < nchunk) {
+    const uint32_t* ph = reinterpret_cast<const uint32_t*>(&mine);
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(&wv);
+    u32x4_t o4;
 #pragma unroll
-  for (int c = 0; c < kNormMaxChunks; ++c) {
-    const int i = threadIdx.x + c * kThreads;
-    if (i < nchunk) {
-      const uint32_t* ph = reinterpret_cast<const uint32_t*>(&hv[c]);
-      const uint32_t* pw = reinterpret_cast<const uint32_t*>(&wv[c]);
-      u32x4_t o4;
+    for (int k = 0; k < 4; ++k)
+      o4[k] = f2bf2(bf2f((uint16_t)ph[k]) * rstd * (1.0f + bf2f((uint16_t)pw[k])),
+                    bf2f((uint16_t)(ph[k] >> 16)) * rstd * (1.0f + bf2f((uint16_t)(pw[k] >> 16))));
+    st_agent16(reinterpret_cast<uint32_t*>(a.xn + (size_t)row * H) + 4 * mi, o4);
+    if (MX) {
+      // H is a multiple of 512, so a wave's 64 chunks are all in range together
+      uint32_t v[4] = {o4[0], o4[1], o4[2], o4[3]}, eb;
+      st_agent(a.xq + (size_t)row * (H >> 3) + mi, mx_quant8(v, eb));
+      // The wave's 64 chunks are the 16 blocks of 4 K steps of 128: block 4 s + kb holds
+      // K quarter kb of step s. Scales are stored per (4 steps, quarter kb) as one dword,
+      // byte s, the operand a projection lane of quarter kb reads for 4 steps at once.
+      const int lane = tid & 63, kb = (lane >> 2) & 3;
+      uint32_t d = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o4[q] = f2bf2(bf2f((uint16_t)ph[q]) * rstd * (1.0f + bf2f((uint16_t)pw[q])),
-                      bf2f((uint16_t)(ph[q] >> 16)) * rstd * (1.0f + bf2f((uint16_t)(pw[q] >> 16))));
-      st_agent16(op + 4 * i, o4);
-      if (MX) {
-        // H is a multiple of 512, so a wave's 64 chunks are all in range together
-        uint32_t v[4] = {o4[0], o4[1], o4[2], o4[3]}, eb;
-        st_agent(a.xq + (size_t)row * (H >> 3) + i, mx_quant8(v, eb));
-        // The wave's 64 chunks are the 16 blocks of 4 K steps of 128: block 4 s + kb holds
-        // K quarter kb of step s. Scales are stored per (4 steps, quarter kb) as one dword,
-        // byte s, the operand a projection lane of quarter kb reads for 4 steps at once.
-        const int lane = threadIdx.x & 63, kb = (lane >> 2) & 3;
-        uint32_t d = 0;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) d |= (uint32_t)__shfl((int)eb, 16 * st + 4 * kb, 64) << (8 * st);
-        if (lane < 16 && (lane & 3) == 0) st_agent(a.xqs + (size_t)row * (H >> 7) + 4 * (i >> 6) + kb, d);
-      }
+      for (int st = 0; st < 4; ++st) d |= (uint32_t)__shfl((int)eb, 16 * st + 4 * kb, 64) << (8 * st);
+      if (lane < 16 && (lane & 3) == 0) st_agent(a.xqs + (size_t)row * (H >> 7) + 4 * (mi >> 6) + kb, d);
     }
   }
   TRACE_POINT(2);
   wait_stores();
   __syncthreads();
-  if (threadIdx.x < kNormCopies && (int)threadIdx.x < a.G) add_agent(sy(a, kSyNorm + threadIdx.x), 1u);
-  // only this workgroup reads the residual row, so it is rewritten after the hand-off;
-  // each thread rewrites only the chunks it read itself
-#pragma unroll
-  for (int c = 0; c < kNormMaxChunks; ++c) {
-    const int i = threadIdx.x + c * kThreads;
-    if (i < nchunk) rp[i] = hv[c];
-  }
+  if (tid < kNormCopies) add_agent(sy(a, kSyNorm + tid), 1u);
+  // The residual row is rewritten with h, each workgroup its own slice. With a residual
+  // input every workgroup of the row reads the whole row first: the rewrite waits until
+  // every norm workgroup has counted itself (so has finished loading).
+  if (a.has_res) wait_count(sy(a, kSyNorm + b % kNormCopies), (uint32_t)(a.R * a.P), sy(a, kSyError), kErrNormWait);
+  if (mi < nchunk) rp[mi] = mine;
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) add_agent(sy(a, kSyNormExit), 1u);
   TRACE_POINT(3);
 }
 
 // ---------------------------------------------------------------------------------------
 // role 2: one split of one 16-channel projection tile
 
-// f32 accumulator of a 16-channel tile -> the tile's split partials, then the tile counts
-// itself done for its key-head group (or for the b|a tiles). D layout of the 16x16 MFMAs:
-// lane l holds channels 4 (l / 16) + i (i = 0..3) of decode row l % 16.
-__device__ __forceinline__ void publish_tile(const Args& a, int t, int s, f32x4_t acc, float (*red)[256]) {
+// A projection workgroup owns one K range of Kr (<= kKr) and either 4 in_proj_qkvz tiles
+// (one per wave, each over the whole range) or one in_proj_ba tile (its 4 waves taking a
+// quarter of the range each). It stages the activations of its K range (the xn slice, or
+// the MXFP4 image of it) in LDS once, so they cross the load path once per workgroup
+// instead of once per tile, and every wave reads its operand from LDS.
+constexpr int kKr = 1024;   // largest K range of a projection workgroup
+constexpr int kXPad = 8;    // bf16 of padding per LDS row, so that the 16 rows start on different banks
+constexpr int kMxRow = kKr / 2 + 16;         // LDS bytes per row of MXFP4 codes (padded)
+constexpr int kMxScBase = GDN_MAX_ROWS * kMxRow;  // LDS byte offset of the MXFP4 scale rows
+
+struct ProjShared {
+  uint16_t xs[GDN_MAX_ROWS][kKr + kXPad];  // the activation slice [decode row][k], or MXFP4 image bytes
+  float red[4][256];
+};
+
+// the 4 waves' accumulators of one tile -> the tile's split partials (fixed-order sum over
+// the waves), then the tile counts itself done. D layout of the 16x16 MFMAs: lane l holds
+// channels 4 (l / 16) + i (i = 0..3) of decode row l % 16.
+__device__ __forceinline__ void publish_reduced(const Args& a, int t, int s, f32x4_t acc, float (*red)[256]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
   const bool isq = t < a.Tq;
 #pragma unroll
@@ -370,11 +392,25 @@ __device__ __forceinline__ void publish_tile(const Args& a, int t, int s, f32x4_
   const int src = (em & 3) * 64 + (em >> 2) * 16 + en;
   const float v = ((red[0][src] + red[1][src]) + red[2][src]) + red[3][src];
   const int ch = (isq ? t * 16 : a.Nq + (t - a.Tq) * 16) + em;  // channel in [qkvz | ba] order
-  if (en < a.R && (isq || ch < a.Nq + a.Nb))
-    st_agent(&a.part[((size_t)en * (a.Nq + a.Nb) + ch) * a.SP + s], v);
+  if (en < a.R && (isq || ch < a.Nq + a.Nb)) st_agent(&a.part[((size_t)s * a.R + en) * (a.Nq + a.Nb) + ch], v);
   wait_stores();
   __syncthreads();
   if (tid == 0) add_agent(sy(a, isq ? sy_group(t * 16 / a.GW) : kSyBa), 1u);
+}
+
+// each wave's own in_proj_qkvz tile -> its split partials; then the 4 tiles (one key-head
+// group never straddles a workgroup's tiles) count as one
+__device__ __forceinline__ void publish_tiles(const Args& a, int t0, int s, f32x4_t acc) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int en = lane & 15;
+  if (en < a.R) {  // the lane's 4 channels are adjacent: one 16-byte store
+    const int ch = (t0 + wave) * 16 + 4 * (lane >> 4);
+    const u32x4_t v = {__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])};
+    st_agent16(reinterpret_cast<uint32_t*>(&a.part[((size_t)s * a.R + en) * (a.Nq + a.Nb) + ch]), v);
+  }
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) add_agent(sy(a, sy_group(t0 * 16 / a.GW)), 1u);
 }
 
 // bf16 weight operand of K step j (32 wide) for this lane: 8 bf16 of row (lane % 16) at
@@ -392,59 +428,80 @@ __device__ __forceinline__ const u32x4_t* wptr(const Args& a, int t, int j, int 
   return reinterpret_cast<const u32x4_t*>((isq ? a.wq : a.wb) + (size_t)row * a.H + 32 * j + 8 * (lane >> 4));
 }
 
-// one split (s of S, nsteps K steps per wave) of a bf16 tile
-template <bool PACKED>
-__device__ void proj_bf16(const Args& a, int gb, int t, int s, int S, int nsteps, float (*red)[256]) {
+// waits for the norm rows, then copies xn[0..R)[k0, k0 + Kr) into LDS
+__device__ __forceinline__ void stage_xn(const Args& a, int gb, int k0, ProjShared& sh) {
+  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)(a.R * a.P), sy(a, kSyError), kErrNormWait);
+  TRACE_POINT(1);
+  // 16-byte chunks: cpr per row (<= 128), so each pass of the workgroup covers rpp >= 2 rows
+  const int cpr = a.Kr >> 3, rpp = kThreads / cpr, r0 = threadIdx.x / cpr, q = threadIdx.x - r0 * cpr;
+  const bool on = r0 < rpp;
+  constexpr int kPass = GDN_MAX_ROWS / 2;
+  // two rounds of up to 4 loads in flight per thread, so the copy keeps few registers
+#pragma unroll 1
+  for (int u0 = 0; u0 < kPass; u0 += 4) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = r0 + (u0 + u) * rpp;
+      if (on && row < a.R) v[u] = *reinterpret_cast<const u32x4_t*>(a.xn + (size_t)row * a.H + k0 + 8 * q);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = r0 + (u0 + u) * rpp;
+      if (on && row < a.R) *reinterpret_cast<u32x4_t*>(&sh.xs[row][8 * q]) = v[u];
+    }
+  }
+  __syncthreads();
+}
+
+// bf16 tiles over the K range [s Kr, (s+1) Kr): with TILES, wave w streams tile t0 + w over
+// the whole range; otherwise the 4 waves stream tile t0, a quarter of the range each
+template <bool PACKED, bool TILES>
+__device__ void proj_bf16(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // K step of iteration i: the workgroup's 4 waves read 4 adjacent steps at every i. Each
-  // workgroup starts at its own point of its K range (a function of the tile and split
-  // only), so that the workgroups streaming at the same moment spread over the HBM
-  // channels instead of all reading the same offset of their regions.
-  const int rot = (t * 7 + s * 3) % nsteps;
-  auto step_of = [&](int i) {
-    const int r = i + rot < nsteps ? i + rot : i + rot - nsteps;
-    return (s * nsteps + r) * 4 + wave;
-  };
+  const int t = TILES ? t0 + wave : t0;
+  const int nsteps = TILES ? a.Kr >> 5 : a.Kr >> 7;
+  const int l0 = TILES ? 0 : wave * nsteps;  // first local K step (32 wide) of this wave
+  const int jg = s * (a.Kr >> 5);            // global K step of the range's start
+  // Each wave starts at its own point of its K range (a function of the tile and split
+  // only), so that the waves streaming at the same moment spread over the HBM channels.
+  const int rot = (t * 7 + s * 3 + wave) % nsteps;
+  auto lstep = [&](int i) { return l0 + (i + rot < nsteps ? i + rot : i + rot - nsteps); };
 
   // weight window: step i lives in register set i % kWin until consumed
   u32x4_t w[kWin];
 #pragma unroll
   for (int u = 0; u < kWin; ++u)
-    if (u < nsteps) w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, step_of(u), lane));
+    if (u < nsteps) w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, jg + lstep(u), lane));
 
-  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)a.R, sy(a, kSyError), kErrNormWait);
-  TRACE_POINT(1);
-
+  stage_xn(a, gb, s * a.Kr, sh);
   const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
-  const uint16_t* xbase = a.xn + (size_t)xrow * a.H + 8 * (lane >> 4);
-  auto xload = [&](int i) { return *reinterpret_cast<const u32x4_t*>(xbase + 32 * step_of(i)); };
-  u32x4_t x[kWin];
-#pragma unroll
-  for (int u = 0; u < kWin; ++u)
-    if (u < nsteps) x[u] = xload(u);
+  auto xload = [&](int i) {
+    return *reinterpret_cast<const u32x4_t*>(&sh.xs[xrow][32 * lstep(i) + 8 * (lane >> 4)]);
+  };
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int i0 = 0; i0 < nsteps; i0 += kWin) {
 #pragma unroll
     for (int u = 0; u < kWin; ++u) {
       const int i = i0 + u;
       if (i < nsteps) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[u]), as_bf16x8(x[u]), acc, 0, 0, 0);
-        if (i + kWin < nsteps) {
-          w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, step_of(i + kWin), lane));
-          x[u] = xload(i + kWin);
-        }
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[u]), as_bf16x8(xload(i)), acc, 0, 0, 0);
+        if (i + kWin < nsteps) w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, jg + lstep(i + kWin), lane));
       }
     }
   }
   TRACE_POINT(2);
-  publish_tile(a, t, s, acc, red);
+  if (TILES)
+    publish_tiles(a, t0, s, acc);
+  else
+    publish_reduced(a, t0, s, acc, sh.red);
   TRACE_POINT(3);
   TRACE_HWID(7);
 }
 
 // MXFP4 tiles work in units of 4 K steps of 128 (512 K): one weight-scale dword and one
 // activation-scale dword per lane cover a unit, byte `st` serving step st of the unit.
-constexpr int kWinMx = 2;  // units each wave keeps in flight (4 KiB of codes per unit)
+constexpr int kWinMx = kKr / 512;  // units of a wave's K range, all kept in flight
 
 struct MxUnit {
   u32x4_t c[4];  // codes of the unit's 4 steps: 32 e2m1 values of this lane's row and K quarter
@@ -473,81 +530,93 @@ __device__ __forceinline__ void mx_wload(const Args& a, int t, int U, int lane, 
   }
 }
 
-__device__ __forceinline__ void mx_xload(const Args& a, int xrow, int U, int lane, MxUnit& m) {
-  const int kb = lane >> 4;
-  const uint8_t* c = reinterpret_cast<const uint8_t*>(a.xq) + (size_t)xrow * (a.H >> 1) + 256 * U + 16 * kb;
+// waits for the norm rows, then copies the MXFP4 image of xn[0..R)[k0, k0 + Kr) into LDS:
+// codes at row * kMxRow, scale dwords (grouped per unit as in the global image) after them
+__device__ __forceinline__ void stage_xq(const Args& a, int gb, int k0, ProjShared& sh) {
+  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)(a.R * a.P), sy(a, kSyError), kErrNormWait);
+  TRACE_POINT(1);
+  uint8_t* lds = reinterpret_cast<uint8_t*>(&sh.xs[0][0]);
+  // 16-byte code chunks: cpr per row (<= 32), rpp >= 8 rows per pass; scale dwords: spr per
+  // row (<= 8), all rows in one pass
+  const int cpr = a.Kr >> 5, rpp = kThreads / cpr, r0 = threadIdx.x / cpr, q = threadIdx.x - r0 * cpr;
+  const int spr = a.Kr >> 7, rs = threadIdx.x / spr, qs = threadIdx.x - rs * spr;
+  constexpr int kPass = GDN_MAX_ROWS / 8;
+  u32x4_t v[kPass];
+  uint32_t sv = 0;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) m.c[st] = *reinterpret_cast<const u32x4_t*>(c + 64 * st);
-  m.sc = a.xqs[(size_t)xrow * (a.H >> 7) + 4 * U + kb];
+  for (int u = 0; u < kPass; ++u) {
+    const int row = r0 + u * rpp;
+    if (row < a.R)
+      v[u] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.xq) + (size_t)row * (a.H >> 1) +
+                                               (k0 >> 1) + 16 * q);
+  }
+  if (rs < a.R) sv = a.xqs[(size_t)rs * (a.H >> 7) + (k0 >> 7) + qs];
+#pragma unroll
+  for (int u = 0; u < kPass; ++u) {
+    const int row = r0 + u * rpp;
+    if (row < a.R) *reinterpret_cast<u32x4_t*>(lds + row * kMxRow + 16 * q) = v[u];
+  }
+  if (rs < a.R) *reinterpret_cast<uint32_t*>(lds + kMxScBase + 4 * (rs * (spr + 1) + qs)) = sv;
+  __syncthreads();
 }
 
 template <int ST>
-__device__ __forceinline__ f32x4_t mx_mfma(const MxUnit& w, const MxUnit& x, f32x4_t acc) {
+__device__ __forceinline__ f32x4_t mx_mfma(const MxUnit& w, const u32x4_t x, uint32_t xs, f32x4_t acc) {
   const i32x8_t A = {(int)w.c[ST][0], (int)w.c[ST][1], (int)w.c[ST][2], (int)w.c[ST][3], 0, 0, 0, 0};
-  const i32x8_t B = {(int)x.c[ST][0], (int)x.c[ST][1], (int)x.c[ST][2], (int)x.c[ST][3], 0, 0, 0, 0};
+  const i32x8_t B = {(int)x[0], (int)x[1], (int)x[2], (int)x[3], 0, 0, 0, 0};
   // formats 4 = e2m1 for both operands; op_sel picks scale byte ST of each scale dword
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 4, ST, (int)w.sc, ST, (int)x.sc);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 4, ST, (int)w.sc, ST, (int)xs);
 }
 
-// one split of an MXFP4 in_proj_qkvz tile: units s * ups .. (s + 1) * ups - 1, wave w taking
-// units w, w + 4, ... of them
+// MXFP4 in_proj_qkvz: wave w streams tile t0 + w over the K range [s Kr, (s+1) Kr)
 template <bool PACKED>
-__device__ void proj_mx(const Args& a, int gb, int t, int s, float (*red)[256]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nu = a.ups > wave ? (a.ups - wave + 3) >> 2 : 0;
-  const int rot = nu ? (t * 7 + s * 3) % nu : 0;  // spread concurrent streams over the channels
-  auto unit_of = [&](int m) {
-    const int r = m + rot < nu ? m + rot : m + rot - nu;
-    return s * a.ups + wave + 4 * r;
-  };
-  MxUnit w[kWinMx], x[kWinMx];
+__device__ void proj_mx(const Args& a, int gb, int t0, int s, ProjShared& sh) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kb = lane >> 4;
+  const int t = t0 + wave;
+  const int nu = a.Kr >> 9, u0 = s * nu;  // units in the range; first global unit
+  const int rot = (t * 7 + s * 3) % nu;   // spread concurrent streams over the channels
+  auto lunit = [&](int m) { return m + rot < nu ? m + rot : m + rot - nu; };
+  MxUnit w[kWinMx];
 #pragma unroll
-  for (int u = 0; u < kWinMx; ++u)
-    if (u < nu) mx_wload<PACKED>(a, t, unit_of(u), lane, w[u]);
+  for (int m = 0; m < kWinMx; ++m)
+    if (m < nu) mx_wload<PACKED>(a, t, u0 + lunit(m), lane, w[m]);
 
-  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)a.R, sy(a, kSyError), kErrNormWait);
-  TRACE_POINT(1);
-
+  stage_xq(a, gb, s * a.Kr, sh);
   const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
-#pragma unroll
-  for (int u = 0; u < kWinMx; ++u)
-    if (u < nu) mx_xload(a, xrow, unit_of(u), lane, x[u]);
+  const uint8_t* lds = reinterpret_cast<const uint8_t*>(&sh.xs[0][0]);
+  const uint8_t* xc = lds + xrow * kMxRow + 16 * kb;
+  const uint32_t* xsc = reinterpret_cast<const uint32_t*>(lds + kMxScBase) + xrow * ((a.Kr >> 7) + 1) + kb;
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int m0 = 0; m0 < nu; m0 += kWinMx) {
 #pragma unroll
-    for (int u = 0; u < kWinMx; ++u) {
-      const int m = m0 + u;
-      if (m < nu) {
-        acc = mx_mfma<0>(w[u], x[u], acc);
-        acc = mx_mfma<1>(w[u], x[u], acc);
-        acc = mx_mfma<2>(w[u], x[u], acc);
-        acc = mx_mfma<3>(w[u], x[u], acc);
-        if (m + kWinMx < nu) {
-          mx_wload<PACKED>(a, t, unit_of(m + kWinMx), lane, w[u]);
-          mx_xload(a, xrow, unit_of(m + kWinMx), lane, x[u]);
-        }
-      }
+  for (int m = 0; m < kWinMx; ++m) {
+    if (m < nu) {
+      const int ul = lunit(m);
+      const uint32_t xs = xsc[4 * ul];
+      acc = mx_mfma<0>(w[m], *reinterpret_cast<const u32x4_t*>(xc + 256 * ul), xs, acc);
+      acc = mx_mfma<1>(w[m], *reinterpret_cast<const u32x4_t*>(xc + 256 * ul + 64), xs, acc);
+      acc = mx_mfma<2>(w[m], *reinterpret_cast<const u32x4_t*>(xc + 256 * ul + 128), xs, acc);
+      acc = mx_mfma<3>(w[m], *reinterpret_cast<const u32x4_t*>(xc + 256 * ul + 192), xs, acc);
     }
   }
   TRACE_POINT(2);
-  publish_tile(a, t, s, acc, red);
+  publish_tiles(a, t0, s, acc);
   TRACE_POINT(3);
   TRACE_HWID(7);
 }
 
-// projection workgroup gb: in_proj_qkvz tiles first (S splits each), then the b|a tiles
-// (Sb splits each)
+// projection workgroup gb: groups of 4 in_proj_qkvz tiles first, then the b|a tiles; S K
+// ranges each
 template <bool PACKED, bool MX>
-__device__ void proj_role(const Args& a, int gb, float (*red)[256]) {
+__device__ void proj_role(const Args& a, int gb, ProjShared& sh) {
   if (gb < a.Gq) {
-    const int t = gb / a.S, s = gb - t * a.S;
+    const int tg = gb / a.S, s = gb - tg * a.S;
     if (MX)
-      proj_mx<PACKED>(a, gb, t, s, red);
+      proj_mx<PACKED>(a, gb, 4 * tg, s, sh);
     else
-      proj_bf16<PACKED>(a, gb, t, s, a.S, a.spw, red);
+      proj_bf16<PACKED, true>(a, gb, 4 * tg, s, sh);
   } else {
-    const int g = gb - a.Gq, tb = g / a.Sb, s = g - tb * a.Sb;
-    proj_bf16<PACKED>(a, gb, a.Tq + tb, s, a.Sb, a.spwb, red);
+    const int g = gb - a.Gq, tb = g / a.S, s = g - tb * a.S;
+    proj_bf16<PACKED, false>(a, gb, a.Tq + tb, s, sh);
   }
 }
 
@@ -585,9 +654,9 @@ struct StateIO<uint16_t> {
 };
 
 struct RecShared {
-  float qs[128], ks[128], vs[128], zs[128], dl[128];
-  float red[1024], red2[1024];  // [row group][column], row groups x dv = 1024 for every head size
-  float scal[8];
+  float y[4][128];                           // projection outputs q, k, v, z of the head (bf16 values)
+  float qs[128], ks[128], vs[128];           // conv outputs q, k, v (SiLU, bf16 values)
+  float scal[4];                             // [2] exp(g), [3] beta
   float bsum[4];
 };
 
@@ -624,43 +693,72 @@ __device__ __forceinline__ void conv_store(const Args& a, int slot, const ConvIn
   st[(size_t)(kConvW - 2) * a.Cd] = f2bf(y);
 }
 
-// The split partials of one channel of row n sit next to each other (SP <= 8 floats), so
-// one or two 16-byte loads fetch them. Plain loads are safe here: a partial line holds
-// channels of one key-head group (or of the b|a tiles) of one row only, nothing reads it
-// before that group's counter completes, and caches start each launch clean.
-constexpr int kMaxSplits = 8;
-struct Partials {
-  f32x4_t p[2];
-};
-__device__ __forceinline__ Partials proj_load(const Args& a, int n, int ch) {
-  const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.part + ((size_t)n * (a.Nq + a.Nb) + ch) * a.SP);
-  Partials r;
-  r.p[0] = src[0];
-  if (a.SP > 4) r.p[1] = src[1];
-  return r;
-}
-// ... added in split order and rounded to bf16: the channel's projection output
-__device__ __forceinline__ float proj_sum(const Partials& r, int splits) {
-  float v = 0.0f;
+// The split partials live split-major ([S, R, Nq + Nb]), so a projection workgroup stores
+// them with 16-byte stores. A reader takes 4 adjacent channels of row n per 16-byte load,
+// S loads in one straight sequence (split indices past S repeat the last one, so the
+// compiler issues them back to back), and adds them in split order. Plain loads are safe
+// here: nothing reads a partial before its tiles' counter completes, and caches start
+// each launch clean.
+constexpr int kMaxSplits = 16;
+template <int N>
+__device__ __forceinline__ f32x4_t sum_splits4(const f32x4_t* base, size_t stride, int S) {
+  f32x4_t p[N];
 #pragma unroll
-  for (int q = 0; q < kMaxSplits; ++q)
-    if (q < splits) v += r.p[q >> 2][q & 3];
-  return rbf(v);
+  for (int q = 0; q < N; ++q) p[q] = base[(size_t)min(q, S - 1) * stride];
+  f32x4_t v = p[0];
+#pragma unroll
+  for (int q = 1; q < N; ++q)
+    if (q < S) v += p[q];
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float sum_splits1(const float* base, size_t stride, int S) {
+  float p[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) p[q] = base[(size_t)min(q, S - 1) * stride];
+  float v = p[0];
+#pragma unroll
+  for (int q = 1; q < N; ++q)
+    if (q < S) v += p[q];
+  return v;
+}
+// projection outputs (bf16 values) of channels ch .. ch + 3 of row n (ch a multiple of 4)
+__device__ __forceinline__ f32x4_t proj_quad(const Args& a, int n, int ch) {
+  const size_t nn = (size_t)(a.Nq + a.Nb);
+  const f32x4_t* base = reinterpret_cast<const f32x4_t*>(a.part + (size_t)n * nn + ch);
+  const size_t stride = a.R * nn / 4;
+  f32x4_t v = a.S <= 4 ? sum_splits4<4>(base, stride, a.S)
+            : a.S <= 8 ? sum_splits4<8>(base, stride, a.S) : sum_splits4<16>(base, stride, a.S);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) v[c] = rbf(v[c]);
+  return v;
+}
+// projection output (a bf16 value) of channel ch of row n
+__device__ __forceinline__ float proj_one(const Args& a, int n, int ch) {
+  const size_t nn = (size_t)(a.Nq + a.Nb);
+  const float* base = a.part + (size_t)n * nn + ch;
+  const size_t stride = a.R * nn;
+  return rbf(a.S <= 4 ? sum_splits1<4>(base, stride, a.S)
+             : a.S <= 8 ? sum_splits1<8>(base, stride, a.S) : sum_splits1<16>(base, stride, a.S));
 }
 
 template <int DK, typename ST>
 __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   constexpr int DV = DK;
-  constexpr int NCQ = DV / 4;          // column quads
-  constexpr int NRG = kThreads / NCQ;  // row groups
-  constexpr int RPT = DK / NRG;        // state rows per thread
-  static_assert(NRG * NCQ == kThreads && RPT * NRG == DK && NRG * DV == 1024 && DK <= 128, "tile shape");
+  // State tile layout: wave w owns the columns [w DV/4, (w+1) DV/4) as QW quads of 4
+  // columns; its 64 lanes are QW quads x NRG row groups, lane = rg * QW + quad, and a lane
+  // holds rows rg + NRG m (m < RPT) of its 4 columns. Sums over the key dim (S^T k, S^T q)
+  // then stay inside a wave: an xor butterfly over the row-group bits of the lane id.
+  constexpr int QW = DV / 16;          // column quads per wave
+  constexpr int NRG = 64 / QW;         // row groups per wave
+  constexpr int RPT = DK / NRG;        // state rows per lane
+  static_assert(QW * NRG == 64 && RPT * NRG == DK && RPT >= 1 && DK <= 128, "tile shape");
   const int n = rb / a.nv, h = rb - n * a.nv, tid = threadIdx.x;
   const int kap = h / a.r, hh = h - kap * a.r;
   const bool qk_owner = hh == a.r - 1;  // writes the key head's q|k conv state
   const int slot = a.idx[n];
   const bool valid = slot > 0 && slot < a.slots;
-  const int cq = tid % NCQ, rg = tid / NCQ;
+  const int lane = tid & 63, rg = lane / QW, cq = (tid >> 6) * QW + lane % QW;
   const size_t sbase = (((size_t)(valid ? slot : 0) * a.nv + h) * DK) * DV + 4 * cq;
 
   // everything that does not depend on this launch's projections is loaded first
@@ -678,7 +776,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
     }
   }
   const float alog = a.A_log[h], dtb = bf2f(a.dt_bias[h]);
-  const float gw = tid < DV ? bf2f(a.gnw[tid]) : 0.0f;
+  const uint2 gw4 = *reinterpret_cast<const uint2*>(a.gnw + 4 * cq);  // gated-norm weights of the 4 columns
   if (valid && !qk_owner) {
     // the old q|k conv rows are in registers: let the owner overwrite them
     wait_stores();
@@ -687,104 +785,108 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   }
 
   // every recurrence workgroup waits, pad rows included (see the counter clearing below)
-  wait_count(sy(a, sy_group(kap)), (uint32_t)(a.GW / 16 * a.S), sy(a, kSyError), kErrGroupWait);
-  wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.Sb), sy(a, kSyError), kErrGroupWait);
+  wait_count(sy(a, sy_group(kap)), (uint32_t)(a.GW / 64 * a.S), sy(a, kSyError), kErrGroupWait);
+  wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.S), sy(a, kSyError), kErrGroupWait);
   TRACE_POINT(1);
 
   uint16_t* core = a.core + (size_t)n * a.nv * DV + (size_t)h * DV;
   uint32_t exit_ticket = 0;
   if (valid) {
     const int gbase = kap * a.GW;
-    // each thread loads the partials of up to two channels, all splits at once
-    const int j = tid - 128;
-    const int ch0 = qk_thread ? gbase + tid : v_thread ? gbase + 2 * DK + hh * DV + j : -1;
-    const int ch1 = qk_thread ? gbase + DK + tid : v_thread ? gbase + 2 * DK + a.r * DV + hh * DV + j : -1;
-    Partials p0, p1, pg;
-    if (ch0 >= 0) p0 = proj_load(a, n, ch0), p1 = proj_load(a, n, ch1);
-    // the two gates are independent chains: thread 64 takes b, thread 65 takes a
-    if (tid == 64 || tid == 65) pg = proj_load(a, n, a.Nq + kap * 2 * a.r + (tid - 64) * a.r + hh);
+    // threads < DK: one quad of the head's channels each, q | k | v | z in DK / 4 quads apiece
+    if (tid < DK) {
+      const int blk = tid / (DK / 4), j = 4 * (tid % (DK / 4));
+      const int ch = gbase + (blk == 0 ? j : blk == 1 ? DK + j : blk == 2 ? 2 * DK + hh * DV + j
+                                                              : 2 * DK + a.r * DV + hh * DV + j);
+      *reinterpret_cast<f32x4_t*>(&sh.y[blk][j]) = proj_quad(a, n, ch);
+    }
+    // the two gates are independent chains: thread 128 takes b, thread 192 takes a
+    float yg = 0.0f;
+    if (tid == 128 || tid == 192) yg = proj_one(a, n, a.Nq + kap * 2 * a.r + (tid == 192 ? a.r : 0) + hh);
     // past every wait of this workgroup: count it (loads complete in issue order, so the
     // atomic goes after this wave's loads to keep its latency off their path)
     if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
     TRACE_POINT(5);
-    float yq = 0.0f, yk = 0.0f;  // this thread's q and k projection outputs (bf16 values)
-    if (qk_thread) {
-      yq = proj_sum(p0, a.S);
-      yk = proj_sum(p1, a.S);
-      sh.qs[tid] = conv_out(c0, yq);
-      sh.ks[tid] = conv_out(c1, yk);
-    } else if (v_thread) {
-      const float yv = proj_sum(p0, a.S);
-      sh.vs[j] = conv_out(c0, yv);
-      sh.zs[j] = proj_sum(p1, a.S);
-      conv_store(a, slot, c0, yv);
-    }
-    if (tid == 64) {
-      sh.scal[3] = __builtin_amdgcn_rcpf(1.0f + __expf(-proj_sum(pg, a.Sb)));  // beta = sigmoid(b)
-    } else if (tid == 65) {
-      const float x = proj_sum(pg, a.Sb) + dtb;
+    if (tid == 128) {
+      sh.scal[3] = __builtin_amdgcn_rcpf(1.0f + __expf(-yg));  // beta = sigmoid(b)
+    } else if (tid == 192) {
+      const float x = yg + dtb;
       const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
       sh.scal[2] = __expf(-__expf(alog) * sp);  // exp(g), g = -exp(A_log) softplus(a + dt_bias)
     }
     __syncthreads();
-    TRACE_POINT(2);
-    // squared norms of q and k and their dot product, over the key head dim
-    if (tid < 64) {
-      float sq = 0.0f, sk = 0.0f, kq = 0.0f;
-      for (int i = tid; i < DK; i += 64) {
-        sq = fmaf(sh.qs[i], sh.qs[i], sq);
-        sk = fmaf(sh.ks[i], sh.ks[i], sk);
-        kq = fmaf(sh.ks[i], sh.qs[i], kq);
-      }
-      sq = wave_sum(sq), sk = wave_sum(sk), kq = wave_sum(kq);
-      if (tid == 0) sh.scal[0] = sq, sh.scal[1] = sk, sh.scal[4] = kq;
+    const int j = tid - 128;
+    float yq = 0.0f, yk = 0.0f;  // this thread's q and k projection outputs (bf16 values)
+    if (qk_thread) {
+      yq = sh.y[0][tid];
+      yk = sh.y[1][tid];
+      sh.qs[tid] = conv_out(c0, yq);
+      sh.ks[tid] = conv_out(c1, yk);
+    } else if (v_thread) {
+      const float yv = sh.y[2][j];
+      sh.vs[j] = conv_out(c0, yv);
+      conv_store(a, slot, c0, yv);
     }
     __syncthreads();
-    TRACE_POINT(6);
-    const float qscale = (1.0f / sqrtf(sh.scal[0] + a.l2eps)) * (1.0f / sqrtf((float)DK));
-    const float kscale = 1.0f / sqrtf(sh.scal[1] + a.l2eps);
-    const float decay = sh.scal[2], beta = sh.scal[3];
-    const float kq = sh.scal[4] * kscale * qscale;  // (normalised k) . (normalised, scaled q)
-
-    // One pass over the old state S: u = S^T k and w = S^T q. With the decay folded in,
-    // the updated state S' = e^g S + k d^T, d = beta (v - e^g u), reads out
-    // o = S'^T q = e^g w + d (k . q); the update itself follows the output.
-    float pu[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    TRACE_POINT(2);
+    // One pass over the old state with the raw (not yet normalised) conv outputs k and q:
+    // per lane, the partial sums over its rows of S^T k and S^T q for its 4 columns and of
+    // k.k, q.q and k.q; then sums over the row groups by an xor butterfly inside the wave,
+    // after which every lane of a column quad holds the same totals.
+    float v[11] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
       const int i = rg + NRG * m;
-      const float kh = sh.ks[i] * kscale, qh = sh.qs[i] * qscale;
+      const float k = sh.ks[i], q = sh.qs[i];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        pu[c] = fmaf(S[m][c], kh, pu[c]);
-        pw[c] = fmaf(S[m][c], qh, pw[c]);
+        v[c] = fmaf(S[m][c], k, v[c]);
+        v[4 + c] = fmaf(S[m][c], q, v[4 + c]);
       }
+      v[8] = fmaf(k, k, v[8]);
+      v[9] = fmaf(q, q, v[9]);
+      v[10] = fmaf(k, q, v[10]);
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sh.red[rg * DV + 4 * cq + c] = pu[c], sh.red2[rg * DV + 4 * cq + c] = pw[c];
-    __syncthreads();
-    float ob = 0.0f;
-    if (tid < DV) {
-      float u = 0.0f, w = 0.0f;
+    for (int mask = QW; mask < 64; mask <<= 1) {
 #pragma unroll
-      for (int q = 0; q < NRG; ++q) u += sh.red[q * DV + tid], w += sh.red2[q * DV + tid];
-      const float d = beta * (sh.vs[tid] - decay * u);
-      sh.dl[tid] = d;
-      ob = rbf(fmaf(d, kq, decay * w));
+      for (int e = 0; e < 11; ++e) v[e] += __shfl_xor(v[e], mask, 64);
     }
-    const float ss = block_sum(tid < DV ? ob * ob : 0.0f, sh.bsum);  // its barriers publish dl
-    TRACE_POINT(7);
-    const float rstd = 1.0f / sqrtf(ss / (float)DV + a.geps);
-    if (tid < DV) core[tid] = f2bf(ob * rstd * gw * silu(sh.zs[tid]));
-    float d[4];
+    TRACE_POINT(6);
+    const float kscale = 1.0f / sqrtf(v[8] + a.l2eps);                                   // 1 / |k|
+    const float qscale = (1.0f / sqrtf(v[9] + a.l2eps)) * (1.0f / sqrtf((float)DK));   // 1 / (|q| sqrt(dk))
+    const float decay = sh.scal[2], beta = sh.scal[3];
+    const float kq = v[10] * kscale * qscale;  // (normalised k) . (normalised, scaled q)
+    // With u = S^T k and w = S^T q of the old state, the updated state
+    // S' = e^g S + k d^T, d = beta (v - e^g u), reads out o = S'^T q = e^g w + d (k . q).
+    float d[4], ob[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) d[c] = sh.dl[4 * cq + c];
+    for (int c = 0; c < 4; ++c) {
+      d[c] = beta * (sh.vs[4 * cq + c] - decay * (v[c] * kscale));
+      ob[c] = rbf(fmaf(d[c], kq, decay * (v[4 + c] * qscale)));
+    }
+    // the state update and its stores go first; the gated norm needs a sum over all columns
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
       const float kh = sh.ks[rg + NRG * m] * kscale;
 #pragma unroll
       for (int c = 0; c < 4; ++c) S[m][c] = fmaf(decay, S[m][c], kh * d[c]);
       StateIO<ST>::store(a.ssm, sbase + (size_t)(rg + NRG * m) * DV, S[m]);
+    }
+    TRACE_POINT(7);
+    // RMSNormGated over the head: the lanes of row group 0 hold each column once
+    float ss = 0.0f;
+    if (rg == 0) ss = (ob[0] * ob[0] + ob[1] * ob[1]) + (ob[2] * ob[2] + ob[3] * ob[3]);
+    ss = block_sum(ss, sh.bsum);
+    const float rstd = 1.0f / sqrtf(ss / (float)DV + a.geps);
+    if (rg == 0) {
+      const float g0 = bf2f((uint16_t)gw4.x), g1 = bf2f((uint16_t)(gw4.x >> 16));
+      const float g2 = bf2f((uint16_t)gw4.y), g3 = bf2f((uint16_t)(gw4.y >> 16));
+      uint2 o;
+      const float* z = &sh.y[3][4 * cq];
+      o.x = f2bf2(ob[0] * rstd * g0 * silu(z[0]), ob[1] * rstd * g1 * silu(z[1]));
+      o.y = f2bf2(ob[2] * rstd * g2 * silu(z[2]), ob[3] * rstd * g3 * silu(z[3]));
+      *reinterpret_cast<uint2*>(core + 4 * cq) = o;
     }
     TRACE_POINT(3);
 
@@ -807,6 +909,11 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   // waiter), so every projection workgroup is past its norm wait, and no recurrence
   // workgroup reads a counter again (the q|k conv counter is cleared by its owner).
   if (tid == 128 && exit_ticket == (uint32_t)(a.R * a.nv - 1)) {
+    // the norm workgroups may still be rewriting residual rows (past their last wait)
+    int it = 0;
+    while (ld_agent(sy(a, kSyNormExit)) < (uint32_t)(a.R * a.P) && ++it <= kSpinLimit) __builtin_amdgcn_s_sleep(4);
+    if (it > kSpinLimit) __hip_atomic_fetch_or(sy(a, kSyError), kErrNormWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_agent(sy(a, kSyNormExit), 0u);
     for (int c = 0; c < kNormCopies; ++c) st_agent(sy(a, kSyNorm + c), 0u);
     st_agent(sy(a, kSyBa), 0u);
     for (int g = 0; g < a.nk; ++g) st_agent(sy(a, sy_group(g)), 0u);
@@ -820,17 +927,18 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
 template <bool PACKED, bool MX, int DK, typename ST>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   __shared__ union {
-    float red[4][256];
+    ProjShared proj;
     RecShared rec;
   } sh;
   const int b = blockIdx.x;
   TRACE_POINT(0);
-  if (b < a.R) {
-    norm_role<MX>(a, b, sh.red[0]);
-  } else if (b < a.R + a.G) {
-    proj_role<PACKED, MX>(a, b - a.R, sh.red);
+  const int nn = a.R * a.P;
+  if (b < nn) {
+    norm_role<MX>(a, b, sh.rec.bsum);
+  } else if (b < nn + a.G) {
+    proj_role<PACKED, MX>(a, b - nn, sh.proj);
   } else {
-    rec_role<DK, ST>(a, b - a.R - a.G, sh.rec);
+    rec_role<DK, ST>(a, b - nn - a.G, sh.rec);
   }
 }
 
@@ -891,8 +999,8 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __re
 struct gdn_block {
   gdn_block_config cfg;
   int device;
-  int nq, nb, cd, tq, tb, t, splits, spw, steps, sync_words;
-  int sb, spwb, ups;  // b|a tile splits and their steps per wave; MXFP4 units per split
+  int nq, nb, cd, tq, tb, t, splits, steps, sync_words;
+  int kr;             // K range of a projection workgroup
   bool mx;
   void* scratch;
   uint16_t* xn;
@@ -911,6 +1019,15 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// K range of a projection workgroup: the largest divisor of H up to kKr in whole units
+// (4 waves x 32-wide bf16 steps, or 512-wide MXFP4 units); 0 if there is none
+int k_range(int H, bool mx) {
+  const int unit = mx ? 512 : 128;
+  for (int kr = kKr; kr >= unit; kr -= unit)
+    if (H % kr == 0) return kr;
+  return 0;
+}
+
 std::string check_config(const gdn_block_config* c) {
   std::string why;
   auto add = [&](const std::string& s) { why += (why.empty() ? "" : "; ") + s; };
@@ -928,6 +1045,12 @@ std::string check_config(const gdn_block_config* c) {
     add("qkvz_format must be GDN_FMT_BF16 or GDN_FMT_MXFP4");
   if (c->qkvz_format == GDN_FMT_MXFP4 && c->hidden % 512 != 0)
     add("MXFP4 in_proj_qkvz needs hidden to be a multiple of 512 (got " + std::to_string(c->hidden) + ")");
+  if (c->hidden > 0 && c->hidden % 256 == 0) {
+    const int kr = k_range(c->hidden, c->qkvz_format == GDN_FMT_MXFP4);
+    if (kr == 0 || c->hidden / kr > kMaxSplits)
+      add("hidden must split into at most " + std::to_string(kMaxSplits) + " K ranges of a multiple of " +
+          (c->qkvz_format == GDN_FMT_MXFP4 ? "512" : "128") + " up to 1024 (got " + std::to_string(c->hidden) + ")");
+  }
   if (c->ssm_state_dtype != GDN_STATE_F32 && c->ssm_state_dtype != GDN_STATE_BF16)
     add("ssm_state_dtype must be GDN_STATE_F32 or GDN_STATE_BF16");
   if (c->has_residual != 0 && c->has_residual != 1) add("has_residual must be 0 or 1");
@@ -992,27 +1115,14 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   b->t = b->tq + b->tb;
   b->steps = H / 32;
   b->mx = cfg->qkvz_format == GDN_FMT_MXFP4;
-  // K splits: at least one projection workgroup per compute unit, each wave keeping a
-  // whole number of K steps. Fewer, longer-streaming workgroups measured better than
-  // more, shorter ones (late-dispatched workgroups stay behind in the memory queues). The
-  // counts depend on the shape only, never on the row count.
-  int S = 1, Sb;
-  if (!b->mx) {
-    while (S < 8 && b->t * S < 256 && b->steps % (4 * 2 * S) == 0) S *= 2;
-    Sb = S;
-  } else {
-    // MXFP4 tiles split by units of 512 K; the bf16 b|a tiles stream 4x the bytes of an
-    // MXFP4 tile per K, so they take up to 4x the splits
-    const int units = H / 512;
-    while (S < 8 && b->tq * S < 256 && units % (2 * S) == 0) S *= 2;
-    Sb = std::min(8, 4 * S);
-    while (Sb > 1 && b->steps % (4 * Sb) != 0) Sb /= 2;
-    b->ups = units / S;
-  }
+  // K ranges: a projection workgroup stages the activations of its range in LDS, so the
+  // range is the largest divisor of H up to kKr in whole units (32-wide bf16 steps grouped
+  // by 4 waves, or 512-wide MXFP4 units). The split count depends on the shape only,
+  // never on the row count.
+  const int kr = k_range(H, b->mx);
+  b->kr = kr;
+  const int S = H / kr;
   b->splits = S;
-  b->spw = b->steps / (4 * S);
-  b->sb = Sb;
-  b->spwb = b->steps / (4 * Sb);
   b->sync_words = (kSyGroup0 + nk + cfg->max_rows * nk) * kLine;
 
   const int R = cfg->max_rows;
@@ -1023,7 +1133,7 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
     return o;
   };
   const size_t o_xn = take((size_t)R * H * 2);
-  const size_t o_part = take((size_t)(std::max(S, Sb) > 4 ? 8 : 4) * R * (b->nq + b->nb) * 4);
+  const size_t o_part = take((size_t)S * R * (b->nq + b->nb) * 4);
   const size_t o_sync = take((size_t)b->sync_words * 4);
   const size_t o_xq = b->mx ? take((size_t)R * H / 2) : 0;
   const size_t o_xqs = b->mx ? take((size_t)R * H / 32) : 0;
@@ -1150,19 +1260,16 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   a.H = c.hidden;
   a.R = rows;
   a.has_res = c.has_residual;
+  a.P = (c.hidden / 8 + kThreads - 1) / kThreads;
   a.T = b->t;
   a.Tq = b->tq;
   a.Tb = b->tb;
   a.Nq = b->nq;
   a.Nb = b->nb;
   a.S = b->splits;
-  a.SP = std::max(b->splits, b->sb) > 4 ? 8 : 4;
-  a.spw = b->spw;
-  a.Sb = b->sb;
-  a.spwb = b->spwb;
-  a.ups = b->ups;
-  a.Gq = b->tq * b->splits;
-  a.G = a.Gq + b->tb * b->sb;
+  a.Kr = b->kr;
+  a.Gq = b->tq / 4 * b->splits;
+  a.G = a.Gq + b->tb * b->splits;
   a.steps = b->steps;
   a.nk = c.num_k_heads;
   a.dk = c.head_k_dim;
@@ -1177,7 +1284,7 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   a.geps = c.gated_norm_eps;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int grid = rows + a.G + rows * c.num_v_heads;
+  const int grid = rows * a.P + a.G + rows * c.num_v_heads;
   if (packed)
     launch<true>(b, a, grid, st);
   else

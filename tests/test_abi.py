@@ -49,6 +49,7 @@ def _cfg(**kw):
 
 @pytest.mark.parametrize("field,value,needle", [
     ("hidden", 100, "hidden"),
+    ("hidden", 15872, "K ranges"),   # 31 x 512: no K range of a multiple of 128 up to 1024 in 16
     ("num_v_heads", 3, "num_v_heads"),
     ("head_k_dim", 48, "head_k_dim"),
     ("head_v_dim", 64, "head_v_dim"),
