@@ -33,6 +33,7 @@ class GdnBlockConfig(ctypes.Structure):
         ("num_state_slots", c_int32), ("max_rows", c_int32), ("qkvz_format", c_int32),
         ("ssm_state_dtype", c_int32), ("has_residual", c_int32),
         ("norm_eps", c_float), ("gated_norm_eps", c_float), ("l2norm_eps", c_float),
+        ("input_normed", c_int32),
     ]
 
 

@@ -20,7 +20,8 @@ def make_config(shape: GdnShape, max_rows: int | None = None) -> abi.GdnBlockCon
         qkvz_format=abi.GDN_FMT_MXFP4 if s.qkvz_format == FMT_MXFP4 else abi.GDN_FMT_BF16,
         ssm_state_dtype=abi.GDN_STATE_BF16 if s.ssm_state_dtype == SSM_BF16 else abi.GDN_STATE_F32,
         has_residual=1 if s.has_residual else 0,
-        norm_eps=s.norm_eps, gated_norm_eps=s.gated_norm_eps, l2norm_eps=s.l2norm_eps)
+        norm_eps=s.norm_eps, gated_norm_eps=s.gated_norm_eps, l2norm_eps=s.l2norm_eps,
+        input_normed=1 if s.input_normed else 0)
 
 
 def _check(t: torch.Tensor, name: str, dtype, shape, device):
@@ -63,7 +64,7 @@ class GdnBlock:
         s, d = self.shape, self.device
         H = s.hidden
         st = abi.GdnBlockWeights()
-        st.norm_w = _check(w.norm_w, "norm_w", torch.bfloat16, (H,), d)
+        st.norm_w = None if s.input_normed else _check(w.norm_w, "norm_w", torch.bfloat16, (H,), d)
         if s.qkvz_format == FMT_MXFP4:
             st.w_qkvz = _check(w.w_qkvz, "w_qkvz", torch.uint8, (s.n_qkvz, H // 2), d)
             st.w_qkvz_scales = _check(w.w_qkvz_scales, "w_qkvz_scales", torch.uint8, (s.n_qkvz, H // 32), d)
@@ -110,7 +111,7 @@ class GdnBlock:
         ws = weights_struct if weights_struct is not None else self.weights_struct(weights)
         ssm_dtype = torch.bfloat16 if s.ssm_state_dtype == SSM_BF16 else torch.float32
         px = _check(x, "x", torch.bfloat16, (R, H), d)
-        pr = _check(residual, "residual", torch.bfloat16, (R, H), d)
+        pr = None if s.input_normed else _check(residual, "residual", torch.bfloat16, (R, H), d)
         pc = _check(conv_state, "conv_state", torch.bfloat16,
                     (s.num_state_slots, s.conv_width - 1, s.conv_dim), d)
         ps = _check(ssm_state, "ssm_state", ssm_dtype,

@@ -37,6 +37,7 @@ class GdnShape:
     norm_eps: float = 1e-6
     gated_norm_eps: float = 1e-6
     l2norm_eps: float = 1e-6
+    input_normed: bool = False   # x is already the norm's output (no residual add, no norm)
     # workload fields: the row counts this shape is exercised at, whether pad
     # rows are mixed in, and how many layer copies a timing run rotates over
     rows: tuple = (1,)
@@ -120,7 +121,17 @@ TP8_RANK_MXFP4 = GdnShape(
     description="one TP8 rank's share, MXFP4 in_proj_qkvz, bf16 state, pad rows",
 )
 
-ALL = {s.name: s for s in (TINY, TP8_RANK_BF16, TP8_RANK_F32, DENSE_FULL, TP8_RANK_MXFP4)}
+# the "normed" variant: the block starts from the norm's output ("SGLang PR #43558",
+# Modifications: K1Build.normed)
+TP8_RANK_BF16_NORMED = TP8_RANK_BF16.with_(
+    name="tp8_rank_bf16_state_normed_input", input_normed=True, rows=(1, 2, 4, 8, 12, 16),
+    description="one TP8 rank's share, bf16 state, input already normed")
+TP8_RANK_MXFP4_NORMED = TP8_RANK_MXFP4.with_(
+    name="tp8_rank_mxfp4_normed_input", input_normed=True, has_residual=False,
+    description="one TP8 rank's share, MXFP4 in_proj_qkvz, input already normed")
+
+ALL = {s.name: s for s in (TINY, TP8_RANK_BF16, TP8_RANK_F32, DENSE_FULL, TP8_RANK_MXFP4,
+                           TP8_RANK_BF16_NORMED, TP8_RANK_MXFP4_NORMED)}
 
 
 def algorithmic_bytes(shape: GdnShape, rows: int, valid_rows: int | None = None) -> int:
@@ -139,7 +150,11 @@ def algorithmic_bytes(shape: GdnShape, rows: int, valid_rows: int | None = None)
         w_qkvz = 2 * H * s.n_qkvz
     w_other = 2 * H * s.n_ba + 2 * H + 2 * s.conv_dim * s.conv_width + 4 * s.num_v_heads \
         + 2 * s.num_v_heads + 2 * s.head_v_dim
-    per_row = 2 * H + (2 * H if s.has_residual else 0) + 2 * H + 2 * s.value_dim
+    if s.input_normed:  # x read, no residual, no norm weight
+        w_other -= 2 * H
+        per_row = 2 * H + 2 * s.value_dim
+    else:
+        per_row = 2 * H + (2 * H if s.has_residual else 0) + 2 * H + 2 * s.value_dim
     ssm_elem = 4 if s.ssm_state_dtype == SSM_F32 else 2
     ssm_slot = ssm_elem * s.num_v_heads * s.head_k_dim * s.head_v_dim
     conv_slot = 2 * (s.conv_width - 1) * s.conv_dim

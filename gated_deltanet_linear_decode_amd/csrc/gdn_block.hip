@@ -220,7 +220,8 @@ struct Args {
   float* part;               // [S, R, Nq + Nb] split partials of the projections
   uint32_t* sync;            // sync word lines
   // sizes
-  int H, R, has_res, P;  // P: norm workgroups per row
+  int H, R, has_res, P;  // P: norm workgroups per row (0 with a normed input)
+  int normed;            // x is already the norm's output xn
   int T, Tq, Tb, Nq, Nb, steps;  // tiles (all, in_proj_qkvz, in_proj_ba), channels, 32-wide K steps of H
   int S, Kr, G, Gq;              // K ranges (splits) of Kr each, projection workgroups, of which
                                  // in_proj_qkvz ones
@@ -454,6 +455,70 @@ __device__ __forceinline__ void stage_xn(const Args& a, int gb, int k0, ProjShar
   __syncthreads();
 }
 
+// A normed input (x is xn): no workgroup waits for another before its first multiply. The
+// projection workgroup issues the loads of its K range of x before its weight loads, so
+// they return first, and stores them to LDS (bf16), or quantises them into the MXFP4 image
+// there ("SGLang PR #43558", Modifications: the normed build, every CTA quantising the
+// rows itself).
+constexpr int kXnChunks = GDN_MAX_ROWS * kKr / 8 / kThreads;  // 16-byte chunks per thread at most
+struct XnIn {
+  u32x4_t v[kXnChunks];
+};
+// bf16: chunk (row r0 + u rpp, column chunk q) per thread, as stage_xn maps them
+__device__ __forceinline__ void xin_issue(const Args& a, int k0, XnIn& in) {
+  const int cpr = a.Kr >> 3, rpp = kThreads / cpr, r0 = threadIdx.x / cpr, q = threadIdx.x - r0 * cpr;
+#pragma unroll
+  for (int u = 0; u < kXnChunks; ++u) {
+    const int row = r0 + u * rpp;
+    if (r0 < rpp && row < a.R) in.v[u] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)row * a.H + k0 + 8 * q);
+  }
+}
+__device__ __forceinline__ void xin_store(const Args& a, const XnIn& in, ProjShared& sh) {
+  const int cpr = a.Kr >> 3, rpp = kThreads / cpr, r0 = threadIdx.x / cpr, q = threadIdx.x - r0 * cpr;
+#pragma unroll
+  for (int u = 0; u < kXnChunks; ++u) {
+    const int row = r0 + u * rpp;
+    if (r0 < rpp && row < a.R) *reinterpret_cast<u32x4_t*>(&sh.xs[row][8 * q]) = in.v[u];
+  }
+  __syncthreads();
+  TRACE_POINT(1);
+}
+// MXFP4: wave w takes the (row, 512-wide unit) pairs w, w + 4, ...; lane l the chunk
+// unit * 64 + l of the pair's row, so a wave's 64 chunks are one unit (the quantiser's
+// layout: 4 lanes per 32-block, 16 blocks per unit)
+constexpr int kXqPairs = GDN_MAX_ROWS * kKr / 512 / 4;  // pairs per wave at most
+__device__ __forceinline__ void xqin_issue(const Args& a, int k0, XnIn& in) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nu = a.Kr >> 9;
+#pragma unroll
+  for (int i = 0; i < kXqPairs; ++i) {
+    const int pr = wave + 4 * i, row = pr / nu, unit = pr - row * nu;
+    if (pr < a.R * nu)
+      in.v[i] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)row * a.H + k0 + 512 * unit + 8 * lane);
+  }
+}
+__device__ __forceinline__ void xqin_store(const Args& a, const XnIn& in, ProjShared& sh) {
+  uint8_t* lds = reinterpret_cast<uint8_t*>(&sh.xs[0][0]);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kb = (lane >> 2) & 3;
+  const int nu = a.Kr >> 9, spr = a.Kr >> 7;
+#pragma unroll
+  for (int i = 0; i < kXqPairs; ++i) {
+    const int pr = wave + 4 * i, row = pr / nu, unit = pr - row * nu;
+    if (pr < a.R * nu) {  // uniform over the wave
+      const uint32_t v[4] = {in.v[i][0], in.v[i][1], in.v[i][2], in.v[i][3]};
+      uint32_t eb;
+      *reinterpret_cast<uint32_t*>(lds + row * kMxRow + 4 * (unit * 64 + lane)) = mx_quant8(v, eb);
+      // block 4 st + kb of the unit is K quarter kb of step st: one dword per quarter, byte st
+      uint32_t d = 0;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) d |= (uint32_t)__shfl((int)eb, 16 * st + 4 * kb, 64) << (8 * st);
+      if (lane < 16 && (lane & 3) == 0)
+        *reinterpret_cast<uint32_t*>(lds + kMxScBase + 4 * (row * (spr + 1) + 4 * unit + kb)) = d;
+    }
+  }
+  __syncthreads();
+  TRACE_POINT(1);
+}
+
 // bf16 tiles over the K range [s Kr, (s+1) Kr): with TILES, wave w streams tile t0 + w over
 // the whole range; otherwise the 4 waves stream tile t0, a quarter of the range each
 template <bool PACKED, bool TILES>
@@ -468,13 +533,18 @@ __device__ void proj_bf16(const Args& a, int gb, int t0, int s, ProjShared& sh) 
   const int rot = (t * 7 + s * 3 + wave) % nsteps;
   auto lstep = [&](int i) { return l0 + (i + rot < nsteps ? i + rot : i + rot - nsteps); };
 
+  XnIn xi;
+  if (a.normed) xin_issue(a, s * a.Kr, xi);
   // weight window: step i lives in register set i % kWin until consumed
   u32x4_t w[kWin];
 #pragma unroll
   for (int u = 0; u < kWin; ++u)
     if (u < nsteps) w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, jg + lstep(u), lane));
 
-  stage_xn(a, gb, s * a.Kr, sh);
+  if (a.normed)
+    xin_store(a, xi, sh);
+  else
+    stage_xn(a, gb, s * a.Kr, sh);
   const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
   auto xload = [&](int i) {
     return *reinterpret_cast<const u32x4_t*>(&sh.xs[xrow][32 * lstep(i) + 8 * (lane >> 4)]);
@@ -576,12 +646,17 @@ __device__ void proj_mx(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   const int nu = a.Kr >> 9, u0 = s * nu;  // units in the range; first global unit
   const int rot = (t * 7 + s * 3) % nu;   // spread concurrent streams over the channels
   auto lunit = [&](int m) { return m + rot < nu ? m + rot : m + rot - nu; };
+  XnIn xi;
+  if (a.normed) xqin_issue(a, s * a.Kr, xi);
   MxUnit w[kWinMx];
 #pragma unroll
   for (int m = 0; m < kWinMx; ++m)
     if (m < nu) mx_wload<PACKED>(a, t, u0 + lunit(m), lane, w[m]);
 
-  stage_xq(a, gb, s * a.Kr, sh);
+  if (a.normed)
+    xqin_store(a, xi, sh);
+  else
+    stage_xq(a, gb, s * a.Kr, sh);
   const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
   const uint8_t* lds = reinterpret_cast<const uint8_t*>(&sh.xs[0][0]);
   const uint8_t* xc = lds + xrow * kMxRow + 16 * kb;
@@ -1054,6 +1129,9 @@ std::string check_config(const gdn_block_config* c) {
   if (c->ssm_state_dtype != GDN_STATE_F32 && c->ssm_state_dtype != GDN_STATE_BF16)
     add("ssm_state_dtype must be GDN_STATE_F32 or GDN_STATE_BF16");
   if (c->has_residual != 0 && c->has_residual != 1) add("has_residual must be 0 or 1");
+  if (c->input_normed != 0 && c->input_normed != 1) add("input_normed must be 0 or 1");
+  if (c->input_normed == 1 && c->has_residual == 1)
+    add("input_normed takes the norm's output as x: has_residual must be 0");
   auto bad_eps = [](float e) { return !(e > 0.0f) || !std::isfinite(e); };
   if (bad_eps(c->norm_eps) || bad_eps(c->gated_norm_eps) || bad_eps(c->l2norm_eps))
     add("every eps must be positive and finite");
@@ -1215,13 +1293,17 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
                     std::to_string(rows) + ")");
   if (!w) return fail(b, GDN_E_INVALID_ARG, "gdn_block_decode: weights must not be NULL");
   const bool packed = w->w_proj_packed != nullptr;
-  const void* scales = (b->mx && !packed) ? w->w_qkvz_scales : w->norm_w;  // checked only when read
-  const void* ptrs[] = {x, residual, conv_state, ssm_state, state_idx, core_out, w->norm_w,
+  const bool normed = c.input_normed == 1;
+  const void* scales = (b->mx && !packed) ? w->w_qkvz_scales : x;  // checked only when read
+  const void* res_p = normed ? x : residual;                     // not read with a normed input
+  const void* nw_p = normed ? x : w->norm_w;
+  const void* ptrs[] = {x, res_p, conv_state, ssm_state, state_idx, core_out, nw_p,
                         packed ? w->w_proj_packed : w->w_qkvz, packed ? w->w_proj_packed : w->w_ba,
                         w->conv_w, w->A_log, w->dt_bias, w->gated_norm_w, scales};
-  const char* names[] = {"x", "residual", "conv_state", "ssm_state", "state_idx", "core_out", "norm_w",
+  const char* names[] = {"x", normed ? "x" : "residual", "conv_state", "ssm_state", "state_idx", "core_out",
+                         normed ? "x" : "norm_w",
                          packed ? "w_proj_packed" : "w_qkvz", packed ? "w_proj_packed" : "w_ba", "conv_w",
-                         "A_log", "dt_bias", "gated_norm_w", (b->mx && !packed) ? "w_qkvz_scales" : "norm_w"};
+                         "A_log", "dt_bias", "gated_norm_w", (b->mx && !packed) ? "w_qkvz_scales" : "x"};
   for (size_t i = 0; i < sizeof(ptrs) / sizeof(ptrs[0]); ++i) {
     if (!ptrs[i]) return fail(b, GDN_E_INVALID_ARG, std::string("gdn_block_decode: ") + names[i] + " is NULL");
     if (!aligned16(ptrs[i]))
@@ -1260,7 +1342,8 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   a.H = c.hidden;
   a.R = rows;
   a.has_res = c.has_residual;
-  a.P = (c.hidden / 8 + kThreads - 1) / kThreads;
+  a.normed = normed ? 1 : 0;
+  a.P = normed ? 0 : (c.hidden / 8 + kThreads - 1) / kThreads;
   a.T = b->t;
   a.Tq = b->tq;
   a.Tb = b->tb;
@@ -1284,7 +1367,7 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   a.geps = c.gated_norm_eps;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int grid = rows * a.P + a.G + rows * c.num_v_heads;
+  const int grid = rows * a.P + a.G + rows * c.num_v_heads;  // no norm workgroups with a normed input
   if (packed)
     launch<true>(b, a, grid, st);
   else

@@ -103,6 +103,11 @@ typedef struct gdn_block_config {
   float norm_eps;          /* Gemma RMSNorm eps (1e-6) */
   float gated_norm_eps;    /* RMSNormGated eps (1e-6) */
   float l2norm_eps;        /* eps inside the q/k L2 norm's square root (1e-6) */
+  int32_t input_normed;    /* 1: x is already the norm's output xn (the "normed" build of
+                              "SGLang PR #43558", Modifications): steps 1 (residual add and
+                              norm) are skipped, residual and norm_w are neither read nor
+                              written (they may be NULL), has_residual must be 0; with MXFP4
+                              each projection workgroup quantises its K range of xn itself */
 } gdn_block_config;
 
 typedef struct gdn_block_weights {

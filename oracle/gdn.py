@@ -325,7 +325,11 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
 
     cfg: hidden, num_k_heads, head_k_dim, num_v_heads, head_v_dim, conv_width,
          ssm_state_dtype ('f32'|'bf16'), has_residual, qkvz_format
-         ('bf16'|'mxfp4'), norm_eps, gated_norm_eps, l2norm_eps.
+         ('bf16'|'mxfp4'), norm_eps, gated_norm_eps, l2norm_eps, and optionally
+         input_normed: x is already the norm's output xn ("SGLang PR #43558",
+         Modifications: the "normed" K1 build starts from input_layernorm's
+         output), so the residual add and the norm are skipped and the
+         residual is neither read nor returned (None).
     weights: norm_w, w_qkvz (bf16 bits [Nqkvz, H] or packed e2m1 [Nqkvz, H/2]),
          w_qkvz_scales (MXFP4 only), w_ba, conv_w, A_log (f32), dt_bias, gated_norm_w.
     x, residual: [R, H] bf16 bits; conv_state [slots, W-1, Cd] bf16 bits;
@@ -340,8 +344,11 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
     R = len(state_idx)
     bf16_state = cfg["ssm_state_dtype"] == "bf16"
 
-    h = residual_add(x, residual, cfg["has_residual"])
-    xn = gemma_rmsnorm(h, weights["norm_w"], cfg["norm_eps"])
+    if cfg.get("input_normed", False):
+        h, xn = None, np.array(x, dtype=np.uint16, copy=True)
+    else:
+        h = residual_add(x, residual, cfg["has_residual"])
+        xn = gemma_rmsnorm(h, weights["norm_w"], cfg["norm_eps"])
     if cfg["qkvz_format"] == "mxfp4":
         y_qkvz = project_mxfp4(weights["w_qkvz"], weights["w_qkvz_scales"], xn)
     else:

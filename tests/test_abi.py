@@ -69,6 +69,12 @@ def test_create_refuses_each_bad_field(field, value, needle):
     assert needle in str(e.value)
 
 
+def test_normed_input_refuses_a_residual_input():
+    with pytest.raises(abi.GdnError) as e:
+        abi.gdn_block_create(_cfg(input_normed=1, has_residual=1))
+    assert e.value.code == abi.GDN_E_UNSUPPORTED and "input_normed" in str(e.value)
+
+
 def test_create_lists_every_reason():
     with pytest.raises(abi.GdnError) as e:
         abi.gdn_block_create(_cfg(hidden=100, conv_width=5, max_rows=40, has_residual=3))

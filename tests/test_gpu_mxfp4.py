@@ -140,3 +140,14 @@ def test_exact_activations_tiny(rows):
 @pytest.mark.parametrize("rows", [3, 16])
 def test_exact_activations_tp8_rank(rows):
     _exact_case(configs.TP8_RANK_MXFP4, rows, 70 + rows)
+
+
+@pytest.mark.parametrize("rows", [1, 6, 16])
+def test_tp8_rank_mxfp4_normed_input(rows):
+    """With a normed input both sides quantise the same bf16 x, so no code can flip: the
+    strict element rule applies."""
+    parity_case(configs.TP8_RANK_MXFP4_NORMED, rows, 51, dev=DEV)
+
+
+def test_tiny_mxfp4_normed_input():
+    parity_case(TINY_MX.with_(name="tiny_mxfp4_normed", input_normed=True, has_residual=False), 9, 52, dev=DEV)

@@ -65,3 +65,16 @@ def test_dense_full_width(rows):
 def test_gated_norm_weight_near_one(name):
     shape = configs.ALL[name]
     _case(shape, min(4, shape.max_rows), 16, stress=True, pads=False)
+
+
+@pytest.mark.parametrize("rows", [1, 7, 16])
+def test_tiny_normed_input(rows):
+    """The block started from the norm's output ("SGLang PR #43558", Modifications)."""
+    shape = configs.TINY.with_(name="tiny_normed", input_normed=True, has_residual=False,
+                               num_state_slots=24, pad_rows=True, rows=(16,))
+    _case(shape, rows, 400 + rows)
+
+
+@pytest.mark.parametrize("rows", [1, 5, 16])
+def test_tp8_rank_normed_input(rows):
+    _case(configs.TP8_RANK_BF16_NORMED.with_(pad_rows=True), rows, 41)

@@ -21,7 +21,8 @@ def _bits(t):
     return u16(t) if t.dtype == torch.bfloat16 else t.numpy().view(np.uint32)
 
 
-@pytest.mark.parametrize("name", ["tiny", "tp8_rank_f32_state_pads", "tp8_rank_mxfp4"])
+@pytest.mark.parametrize("name", ["tiny", "tp8_rank_f32_state_pads", "tp8_rank_mxfp4",
+                                  "tp8_rank_mxfp4_normed_input"])
 def test_batch_invariance(name):
     """A probe row's outputs do not change with the other rows or the width."""
     shape = configs.ALL[name].with_(num_state_slots=40, rows=(16,), pad_rows=False)

@@ -13,7 +13,7 @@ import pytest
 
 from gated_deltanet_linear_decode_amd import configs, synth
 from oracle import gdn as og
-from tests.helpers import oracle_cfg, oracle_state, oracle_weights, run_oracle, u16
+from tests.helpers import from_u16, oracle_cfg, oracle_state, oracle_weights, run_oracle, u16
 
 
 def test_pad_rows_write_nothing_but_the_residual():
@@ -185,3 +185,19 @@ def test_block_against_library_composition(bf16_state):
     ref_S = og.bf16_to_f64(og.f64_to_bf16(S_all.numpy())) if bf16_state \
         else S_all.numpy().astype(np.float32).astype(np.float64)
     assert np.allclose(got_S, ref_S, rtol=0, atol=1e-7 if not bf16_state else 0)
+
+
+def test_normed_input_equals_the_block_from_its_norm_output():
+    """The "normed" variant ("SGLang PR #43558", Modifications): fed the xn the full block
+    computes from (x, residual), it gives the same core and state bit for bit, and
+    returns no residual."""
+    shape = configs.TINY.with_(num_state_slots=12, pad_rows=True, rows=(6,))
+    w = synth.make_weights(shape, 90)
+    call = synth.make_call(shape, 6, 90)
+    full = run_oracle(shape, w, call)
+    normed_call = synth.GdnCall(from_u16(full["xn"]), call.residual, call.conv_state, call.ssm_state,
+                                call.state_idx)
+    normed = run_oracle(shape.with_(input_normed=True, has_residual=False), w, normed_call)
+    assert normed["residual"] is None
+    for k in ("core", "conv_state", "ssm_state", "y_qkvz", "y_ba"):
+        assert np.array_equal(normed[k], full[k]), k
