@@ -66,14 +66,17 @@ class Rotation:
                 x=self.call_cpu.x.to(dev).clone(), res=self.call_cpu.residual.to(dev).clone(),
                 conv=self.call_cpu.conv_state.to(dev).clone(), ssm=self.call_cpu.ssm_state.to(dev).clone(),
                 idx=self.call_cpu.state_idx.to(dev).clone(),
-                core=torch.empty(max_rows, shape.value_dim, dtype=torch.bfloat16, device=dev))
+                core=torch.empty(max_rows, shape.value_dim, dtype=torch.bfloat16, device=dev),
+                out=(torch.empty(max_rows, shape.hidden, dtype=torch.bfloat16, device=dev)
+                     if shape.fold_out_proj else None))
             self.copies.append(c)
         torch.cuda.synchronize()
 
     def launch(self, i, rows, packed):
         c = self.copies[i % len(self.copies)]
         self.blk.decode(c["x"][:rows], c["res"][:rows], None, c["conv"], c["ssm"], c["idx"][:rows],
-                        c["core"][:rows], weights_struct=c["wsp"] if packed else c["ws"])
+                        c["core"][:rows], weights_struct=c["wsp"] if packed else c["ws"],
+                        out=c["out"][:rows] if c["out"] is not None else None)
 
     def graph(self, n, rows, packed):
         import torch
@@ -195,7 +198,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workloads", default="tp8_rank_f32_state_pads,dense_full_width,tp8_rank_mxfp4,"
-                    "tp8_rank_bf16_state_normed_input,tp8_rank_mxfp4_normed_input",
+                    "tp8_rank_bf16_state_normed_input,tp8_rank_mxfp4_normed_input,tp8_rank_bf16_state_out_proj",
                     help="other workloads to sweep (tiled weights) after the headline; '' for none")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (HBM counter calibration) and exit")

@@ -23,7 +23,7 @@ GDN_MAX_ROWS = 16
 
 EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error",
             "gdn_block_packed_weight_bytes", "gdn_block_pack_weights", "gdn_block_check",
-            "gdn_mxfp4_quantize")
+            "gdn_mxfp4_quantize", "gdn_block_decode_with_out_proj")
 
 
 class GdnBlockConfig(ctypes.Structure):
@@ -33,7 +33,7 @@ class GdnBlockConfig(ctypes.Structure):
         ("num_state_slots", c_int32), ("max_rows", c_int32), ("qkvz_format", c_int32),
         ("ssm_state_dtype", c_int32), ("has_residual", c_int32),
         ("norm_eps", c_float), ("gated_norm_eps", c_float), ("l2norm_eps", c_float),
-        ("input_normed", c_int32),
+        ("input_normed", c_int32), ("fold_out_proj", c_int32),
     ]
 
 
@@ -41,7 +41,7 @@ class GdnBlockWeights(ctypes.Structure):
     _fields_ = [
         ("norm_w", c_void_p), ("w_qkvz", c_void_p), ("w_qkvz_scales", c_void_p), ("w_ba", c_void_p),
         ("conv_w", c_void_p), ("A_log", c_void_p), ("dt_bias", c_void_p), ("gated_norm_w", c_void_p),
-        ("w_proj_packed", c_void_p),
+        ("w_proj_packed", c_void_p), ("w_out", c_void_p),
     ]
 
 
@@ -79,6 +79,10 @@ def load() -> ctypes.CDLL:
         lib.gdn_block_pack_weights.restype = c_int
         lib.gdn_block_check.argtypes = [c_void_p, POINTER(c_uint32)]
         lib.gdn_block_check.restype = c_int
+        lib.gdn_block_decode_with_out_proj.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(GdnBlockWeights),
+                                                       c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                                       c_void_p]
+        lib.gdn_block_decode_with_out_proj.restype = c_int
         lib.gdn_mxfp4_quantize.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
         lib.gdn_mxfp4_quantize.restype = c_int
         _lib = lib
@@ -101,6 +105,15 @@ def gdn_block_decode(handle, x: int, residual: int, weights: GdnBlockWeights, co
                      ssm_state: int, state_idx: int, rows: int, core_out: int, stream: int) -> None:
     rc = load().gdn_block_decode(handle, x, residual, ctypes.byref(weights), conv_state, ssm_state,
                                  state_idx, rows, core_out, stream)
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(handle))
+
+
+def gdn_block_decode_with_out_proj(handle, x: int, residual: int, weights: GdnBlockWeights, conv_state: int,
+                                   ssm_state: int, state_idx: int, rows: int, core_out: int, out: int,
+                                   stream: int) -> None:
+    rc = load().gdn_block_decode_with_out_proj(handle, x, residual, ctypes.byref(weights), conv_state, ssm_state,
+                                               state_idx, rows, core_out, out, stream)
     if rc != GDN_OK:
         raise GdnError(rc, gdn_block_last_error(handle))
 

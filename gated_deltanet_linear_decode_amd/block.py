@@ -21,7 +21,7 @@ def make_config(shape: GdnShape, max_rows: int | None = None) -> abi.GdnBlockCon
         ssm_state_dtype=abi.GDN_STATE_BF16 if s.ssm_state_dtype == SSM_BF16 else abi.GDN_STATE_F32,
         has_residual=1 if s.has_residual else 0,
         norm_eps=s.norm_eps, gated_norm_eps=s.gated_norm_eps, l2norm_eps=s.l2norm_eps,
-        input_normed=1 if s.input_normed else 0)
+        input_normed=1 if s.input_normed else 0, fold_out_proj=1 if s.fold_out_proj else 0)
 
 
 def _check(t: torch.Tensor, name: str, dtype, shape, device):
@@ -77,6 +77,7 @@ class GdnBlock:
         st.dt_bias = _check(w.dt_bias, "dt_bias", torch.bfloat16, (s.num_v_heads,), d)
         st.gated_norm_w = _check(w.gated_norm_w, "gated_norm_w", torch.bfloat16, (s.head_v_dim,), d)
         st.w_proj_packed = None
+        st.w_out = _check(w.w_out, "w_out", torch.bfloat16, (H, s.value_dim), d) if s.fold_out_proj else None
         return st
 
     def pack(self, w, stream=None) -> torch.Tensor:
@@ -100,8 +101,11 @@ class GdnBlock:
         return abi.gdn_block_check(self.handle)
 
     def decode(self, x, residual, weights, conv_state, ssm_state, state_idx, core_out, rows=None,
-               stream=None, weights_struct=None):
+               stream=None, weights_struct=None, out=None):
         """Enqueue one decode step on `stream` (default: torch's current stream).
+
+        With a shape that folds out_proj, `out` ([R, H] bf16) receives the rank's out_proj
+        partial.
 
         `weights` is a GdnWeights on the device, or pass a prepared
         `weights_struct` (from weights_struct()) to skip re-checking."""
@@ -120,4 +124,8 @@ class GdnBlock:
         po = _check(core_out, "core_out", torch.bfloat16, (R, s.value_dim), d)
         if stream is None:
             stream = torch.cuda.current_stream(d).cuda_stream
-        abi.gdn_block_decode(self.handle, px, pr, ws, pc, ps, pi, R, po, stream)
+        if s.fold_out_proj:
+            pout = _check(out, "out", torch.bfloat16, (R, H), d)
+            abi.gdn_block_decode_with_out_proj(self.handle, px, pr, ws, pc, ps, pi, R, po, pout, stream)
+        else:
+            abi.gdn_block_decode(self.handle, px, pr, ws, pc, ps, pi, R, po, stream)

@@ -38,6 +38,7 @@ class GdnShape:
     gated_norm_eps: float = 1e-6
     l2norm_eps: float = 1e-6
     input_normed: bool = False   # x is already the norm's output (no residual add, no norm)
+    fold_out_proj: bool = False  # also write the out_proj partial [R, H] from the core rows
     # workload fields: the row counts this shape is exercised at, whether pad
     # rows are mixed in, and how many layer copies a timing run rotates over
     rows: tuple = (1,)
@@ -130,8 +131,14 @@ TP8_RANK_MXFP4_NORMED = TP8_RANK_MXFP4.with_(
     name="tp8_rank_mxfp4_normed_input", input_normed=True, has_residual=False,
     description="one TP8 rank's share, MXFP4 in_proj_qkvz, input already normed")
 
+# out_proj folded in: the launch also writes the rank's out_proj partial ("SGLang PR
+# #43558", Modifications: K1 with the out_proj fold)
+TP8_RANK_BF16_OUT = TP8_RANK_BF16.with_(
+    name="tp8_rank_bf16_state_out_proj", fold_out_proj=True, rows=(1, 2, 4, 8, 12, 16),
+    description="one TP8 rank's share, bf16 state, out_proj partial folded in")
+
 ALL = {s.name: s for s in (TINY, TP8_RANK_BF16, TP8_RANK_F32, DENSE_FULL, TP8_RANK_MXFP4,
-                           TP8_RANK_BF16_NORMED, TP8_RANK_MXFP4_NORMED)}
+                           TP8_RANK_BF16_NORMED, TP8_RANK_MXFP4_NORMED, TP8_RANK_BF16_OUT)}
 
 
 def algorithmic_bytes(shape: GdnShape, rows: int, valid_rows: int | None = None) -> int:
@@ -155,6 +162,9 @@ def algorithmic_bytes(shape: GdnShape, rows: int, valid_rows: int | None = None)
         per_row = 2 * H + 2 * s.value_dim
     else:
         per_row = 2 * H + (2 * H if s.has_residual else 0) + 2 * H + 2 * s.value_dim
+    if s.fold_out_proj:  # W_out [H, nv*dv] bf16, and the partial [R, H] bf16 written
+        w_other += 2 * H * s.value_dim
+        per_row += 2 * H
     ssm_elem = 4 if s.ssm_state_dtype == SSM_F32 else 2
     ssm_slot = ssm_elem * s.num_v_heads * s.head_k_dim * s.head_v_dim
     conv_slot = 2 * (s.conv_width - 1) * s.conv_dim

@@ -76,6 +76,7 @@ constexpr int kLine = 32;          // uint32 words per 128-byte line: one hot co
 constexpr int kWin = GDN_WINDOW;
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kNormCopies = 8;     // the norm-done counter is kept on 8 lines, polled spread out
+constexpr int kCoreCopies = 16;    // so is the core-done counter of the out_proj fold, on 16
 
 // ---------------------------------------------------------------------------------------
 // scalar helpers
@@ -186,9 +187,21 @@ __device__ unsigned long long g_trace[kTraceBlocks * kTraceSlots];
 
 // sync word lines (one 128-byte line each): norm workgroups done (kNormCopies copies,
 // polled spread out); b|a tile splits done; recurrence workgroups finished; the sticky
-// error word; norm workgroups finished; then per key-head group: tile splits done; then
-// per (row, key-head group): value heads that have read the old q|k conv rows.
-enum { kSyNorm = 0, kSyBa = kNormCopies, kSyExit, kSyError, kSyNormExit, kSyGroup0 };
+// error word; norm workgroups finished; out_proj workgroups past their wait and (on
+// kCoreCopies lines) recurrence workgroups whose core rows are stored (out_proj fold);
+// then per key-head group: tile splits done; then per (row, key-head group): value heads
+// that have read the old q|k conv rows.
+enum {
+  kSyNorm = 0,
+  kSyBa = kNormCopies,
+  kSyExit,
+  kSyError,
+  kSyNormExit,
+  kSyOutExit,  // top line of the out_proj workgroups' two-level exit count
+  kSyCoreDone,
+  kSyOutExit1 = kSyCoreDone + kCoreCopies,  // its first level, kCoreCopies lines
+  kSyGroup0 = kSyOutExit1 + kCoreCopies
+};
 enum : uint32_t { kErrNormWait = 1u, kErrGroupWait = 2u, kErrConvWait = 4u };
 
 // ---------------------------------------------------------------------------------------
@@ -213,6 +226,9 @@ struct Args {
   const uint16_t* dt_bias;   // [nv]
   const uint16_t* gnw;       // [dv]
   uint16_t* core;            // [R, nv*dv]
+  const uint16_t* wo;        // out_proj [H, nv*dv] (row-major path, fold only)
+  const uint16_t* wo_pk;     // out_proj tiles (packed path, fold only)
+  uint16_t* out;             // [R, H] the out_proj partial (fold only)
   // scratch
   uint16_t* xn;              // [R, H]
   uint32_t* xq;              // MXFP4 image of xn: codes [R, H/2] bytes
@@ -222,6 +238,7 @@ struct Args {
   // sizes
   int H, R, has_res, P;  // P: norm workgroups per row (0 with a normed input)
   int normed;            // x is already the norm's output xn
+  int fold, O, Ko;       // out_proj folded in; its workgroups (4 16-column tiles of H each); K = nv*dv
   int T, Tq, Tb, Nq, Nb, steps;  // tiles (all, in_proj_qkvz, in_proj_ba), channels, 32-wide K steps of H
   int S, Kr, G, Gq;              // K ranges (splits) of Kr each, projection workgroups, of which
                                  // in_proj_qkvz ones
@@ -957,11 +974,14 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
     if (rg == 0) {
       const float g0 = bf2f((uint16_t)gw4.x), g1 = bf2f((uint16_t)(gw4.x >> 16));
       const float g2 = bf2f((uint16_t)gw4.y), g3 = bf2f((uint16_t)(gw4.y >> 16));
-      uint2 o;
       const float* z = &sh.y[3][4 * cq];
-      o.x = f2bf2(ob[0] * rstd * g0 * silu(z[0]), ob[1] * rstd * g1 * silu(z[1]));
-      o.y = f2bf2(ob[2] * rstd * g2 * silu(z[2]), ob[3] * rstd * g3 * silu(z[3]));
-      *reinterpret_cast<uint2*>(core + 4 * cq) = o;
+      const uint64_t o = (uint64_t)f2bf2(ob[0] * rstd * g0 * silu(z[0]), ob[1] * rstd * g1 * silu(z[1])) |
+                         ((uint64_t)f2bf2(ob[2] * rstd * g2 * silu(z[2]), ob[3] * rstd * g3 * silu(z[3])) << 32);
+      uint64_t* dst = reinterpret_cast<uint64_t*>(core + 4 * cq);
+      if (a.fold)  // read by the out_proj workgroups: coherent at agent scope
+        __hip_atomic_store(dst, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        *dst = o;
     }
     TRACE_POINT(3);
 
@@ -976,7 +996,13 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
     }
   } else {
     if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
-    for (int j = tid; j < DV; j += kThreads) core[j] = 0;  // pad row: a zero core row
+    // pad row: a zero core row
+    for (int j = 2 * tid; j < DV; j += 2 * kThreads) st_agent(reinterpret_cast<uint32_t*>(core + j), 0u);
+  }
+  if (a.fold) {  // the core row of this head is in place for the out_proj workgroups
+    wait_stores();
+    __syncthreads();
+    if (tid < kCoreCopies) add_agent(sy(a, kSyCoreDone + tid), 1u);
   }
 
   // The last recurrence workgroup past its waits clears the counters for the next launch:
@@ -998,8 +1024,92 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
 }
 
 // ---------------------------------------------------------------------------------------
+// role 4 (out_proj folded in): the rank's out_proj partial out = bf16(core W_out^T) for 4
+// 16-column tiles of H, one per wave over the whole K = nv*dv (<= 1024). Each wave issues
+// its whole tile (up to 32 KiB, held in registers) before waiting, so the out_proj weights
+// stream while the recurrence runs; a wave's loads return in issue order, so that is all
+// it has in flight when it polls. Then the core rows are staged in LDS once per workgroup
+// and multiplied on the bf16 MFMA ("SGLang PR #43558", Modifications: K1 with the out_proj
+// fold writes the rank's out_proj partial).
+constexpr int kOutSteps = 32;  // 32-wide K steps of a tile at most (K <= 1024)
+template <bool PACKED>
+__device__ void oproj_role(const Args& a, int ob, ProjShared& sh) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int K = a.Ko, nsteps = K >> 5, t = 4 * ob + wave;
+  auto wop = [&](int j) -> const u32x4_t* {
+    if (PACKED)
+      return reinterpret_cast<const u32x4_t*>(a.wo_pk + (((size_t)t * nsteps + j) * 64 + lane) * 8);
+    return reinterpret_cast<const u32x4_t*>(a.wo + (size_t)(t * 16 + (lane & 15)) * K + 32 * j + 8 * (lane >> 4));
+  };
+  u32x4_t w[kOutSteps];
+#pragma unroll
+  for (int u = 0; u < kOutSteps; ++u)
+    if (u < nsteps) w[u] = __builtin_nontemporal_load(wop(u));
 
-template <bool PACKED, bool MX, int DK, typename ST>
+  wait_count(sy(a, kSyCoreDone + ob % kCoreCopies), (uint32_t)(a.R * a.nv), sy(a, kSyError), kErrGroupWait);
+  TRACE_POINT(1);
+  // core rows [R, K] into LDS with direct-to-LDS loads, all in flight at once (plain
+  // loads: first read after the count). One wave instruction fills 1 KiB of LDS, 16 bytes
+  // per lane in lane order, so the image is unpadded [R][K]; to keep the B-operand reads
+  // free of bank conflicts the 16-byte chunk c of row r sits at chunk c ^ (r % 16) of its
+  // row (K is a multiple of 128, so the swizzle stays inside the row).
+  const int cpr = K >> 3, nch = a.R * cpr;
+  char* img = reinterpret_cast<char*>(&sh.xs[0][0]);
+#pragma unroll
+  for (int u = 0; u < GDN_MAX_ROWS * kKr / 8 / 64 / 4; ++u) {
+    const int f0 = 64 * (4 * u + wave), f = f0 + lane;
+    if (f0 < nch) {
+      const int row = f / cpr, c = (f - row * cpr) ^ (row & 15);
+      if (f < nch)
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(a.core + (size_t)row * K + 8 * c),
+                                         (__attribute__((address_space(3))) void*)(img + 16 * f0), 16, 0, 0);
+    }
+  }
+  wait_stores();  // vmcnt(0): this wave's LDS writes have landed
+  __syncthreads();
+  const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
+  const char* xr = img + (size_t)xrow * K * 2;
+  f32x4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+#pragma unroll
+  for (int u = 0; u < kOutSteps; u += 2) {
+    if (u < nsteps) {
+      const int c0 = (4 * u + (lane >> 4)) ^ (xrow & 15), c1 = (4 * (u + 1) + (lane >> 4)) ^ (xrow & 15);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          as_bf16x8(w[u]), as_bf16x8(*reinterpret_cast<const u32x4_t*>(xr + 16 * c0)), acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          as_bf16x8(w[u + 1]), as_bf16x8(*reinterpret_cast<const u32x4_t*>(xr + 16 * c1)), acc1, 0, 0, 0);
+    }
+  }
+  const f32x4_t acc = acc0 + acc1;
+  TRACE_POINT(2);
+  // D layout: lane l holds output columns 4 (l / 16) + i of decode row l % 16
+  const int en = lane & 15;
+  if (en < a.R) {
+    uint16_t* o = a.out + (size_t)en * a.H + t * 16 + 4 * (lane >> 4);
+    *reinterpret_cast<uint2*>(o) = make_uint2(f2bf2(acc[0], acc[1]), f2bf2(acc[2], acc[3]));
+  }
+  TRACE_POINT(3);
+  // The last out_proj workgroup clears the fold's counters for the next launch, counted in
+  // two levels so that no counter line takes more than a few atomics: the last of each of
+  // the L first-level lines counts on the top line.
+  if (tid == 0) {
+    const int L = min(kCoreCopies, a.O), line = ob % L, per = (a.O - line + L - 1) / L;
+    if (add_agent(sy(a, kSyOutExit1 + line), 1u) == (uint32_t)(per - 1) &&
+        add_agent(sy(a, kSyOutExit), 1u) == (uint32_t)(L - 1)) {
+      for (int c = 0; c < kCoreCopies; ++c) {
+        st_agent(sy(a, kSyCoreDone + c), 0u);
+        st_agent(sy(a, kSyOutExit1 + c), 0u);
+      }
+      st_agent(sy(a, kSyOutExit), 0u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+
+// FOLD is a template flag, not only a launch argument, so that the out_proj role's register
+// tile does not raise the register count (and lower the occupancy) of the launches without it.
+template <bool PACKED, bool MX, int DK, typename ST, bool FOLD>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   __shared__ union {
     ProjShared proj;
@@ -1007,13 +1117,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   } sh;
   const int b = blockIdx.x;
   TRACE_POINT(0);
-  const int nn = a.R * a.P;
+  const int nn = a.R * a.P, nr = a.R * a.nv;
   if (b < nn) {
     norm_role<MX>(a, b, sh.rec.bsum);
   } else if (b < nn + a.G) {
     proj_role<PACKED, MX>(a, b - nn, sh.proj);
-  } else {
+  } else if (b < nn + a.G + nr) {
     rec_role<DK, ST>(a, b - nn - a.G, sh.rec);
+  } else if (FOLD) {
+    oproj_role<PACKED>(a, b - nn - a.G - nr, sh.proj);
   }
 }
 
@@ -1076,6 +1188,8 @@ struct gdn_block {
   int device;
   int nq, nb, cd, tq, tb, t, splits, steps, sync_words;
   int kr;             // K range of a projection workgroup
+  bool fold;          // out_proj folded in
+  int o, ko;          // out_proj workgroups (4 tiles of 16 columns of H each) and K (nv * dv)
   bool mx;
   void* scratch;
   uint16_t* xn;
@@ -1132,6 +1246,13 @@ std::string check_config(const gdn_block_config* c) {
   if (c->input_normed != 0 && c->input_normed != 1) add("input_normed must be 0 or 1");
   if (c->input_normed == 1 && c->has_residual == 1)
     add("input_normed takes the norm's output as x: has_residual must be 0");
+  if (c->fold_out_proj != 0 && c->fold_out_proj != 1) add("fold_out_proj must be 0 or 1");
+  if (c->fold_out_proj == 1) {
+    const long long kv = (long long)c->num_v_heads * c->head_v_dim;
+    if (kv % 128 != 0 || kv > 1024)
+      add("fold_out_proj needs num_v_heads * head_v_dim to be a multiple of 128 up to 1024 (got " +
+          std::to_string(kv) + ")");
+  }
   auto bad_eps = [](float e) { return !(e > 0.0f) || !std::isfinite(e); };
   if (bad_eps(c->norm_eps) || bad_eps(c->gated_norm_eps) || bad_eps(c->l2norm_eps))
     add("every eps must be positive and finite");
@@ -1143,12 +1264,20 @@ int fail(gdn_block* b, int code, const std::string& msg) {
   return code;
 }
 
+template <bool PACKED, bool MX, int DK, typename ST>
+void launch_st(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
+  if (b->fold)
+    hipLaunchKernelGGL((decode_kernel<PACKED, MX, DK, ST, true>), dim3(grid), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<PACKED, MX, DK, ST, false>), dim3(grid), dim3(kThreads), 0, st, a);
+}
+
 template <bool PACKED, bool MX, int DK>
 void launch_dk(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
   if (b->cfg.ssm_state_dtype == GDN_STATE_F32)
-    hipLaunchKernelGGL((decode_kernel<PACKED, MX, DK, float>), dim3(grid), dim3(kThreads), 0, st, a);
+    launch_st<PACKED, MX, DK, float>(b, a, grid, st);
   else
-    hipLaunchKernelGGL((decode_kernel<PACKED, MX, DK, uint16_t>), dim3(grid), dim3(kThreads), 0, st, a);
+    launch_st<PACKED, MX, DK, uint16_t>(b, a, grid, st);
 }
 
 template <bool PACKED, bool MX>
@@ -1193,6 +1322,9 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   b->t = b->tq + b->tb;
   b->steps = H / 32;
   b->mx = cfg->qkvz_format == GDN_FMT_MXFP4;
+  b->fold = cfg->fold_out_proj == 1;
+  b->o = H / 64;
+  b->ko = nv * dv;
   // K ranges: a projection workgroup stages the activations of its range in LDS, so the
   // range is the largest divisor of H up to kKr in whole units (32-wide bf16 steps grouped
   // by 4 waves, or 512-wide MXFP4 units). The split count depends on the shape only,
@@ -1244,11 +1376,13 @@ size_t packed_qkvz_bytes(const gdn_block* b) {
   return b->mx ? (size_t)b->nq * H / 2 : (size_t)b->tq * 16 * H * 2;
 }
 size_t packed_scale_bytes(const gdn_block* b) { return b->mx ? (size_t)b->nq * b->cfg.hidden / 32 : 0; }
+size_t packed_ba_bytes(const gdn_block* b) { return (size_t)b->tb * 16 * b->cfg.hidden * 2; }
+size_t packed_out_bytes(const gdn_block* b) { return b->fold ? (size_t)b->cfg.hidden * b->ko * 2 : 0; }
 }  // namespace
 
 extern "C" size_t gdn_block_packed_weight_bytes(gdn_block_t b) {
   if (!b) return 0;
-  return packed_qkvz_bytes(b) + packed_scale_bytes(b) + (size_t)b->tb * 16 * b->cfg.hidden * 2;
+  return packed_qkvz_bytes(b) + packed_scale_bytes(b) + packed_ba_bytes(b) + packed_out_bytes(b);
 }
 
 extern "C" int gdn_block_pack_weights(gdn_block_t b, const gdn_block_weights* w, void* packed, void* stream) {
@@ -1257,6 +1391,8 @@ extern "C" int gdn_block_pack_weights(gdn_block_t b, const gdn_block_weights* w,
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w, w->w_qkvz, w->w_ba and packed must not be NULL");
   if (b->mx && !w->w_qkvz_scales)
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w->w_qkvz_scales must not be NULL for MXFP4");
+  if (b->fold && (!w->w_out || !aligned16(w->w_out)))
+    return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w->w_out must be a 16-byte aligned pointer (fold_out_proj)");
   if (!aligned16(w->w_qkvz) || !aligned16(w->w_ba) || !aligned16(packed) ||
       (b->mx && !aligned16(w->w_qkvz_scales)))
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: pointers must be 16-byte aligned");
@@ -1277,21 +1413,31 @@ extern "C" int gdn_block_pack_weights(gdn_block_t b, const gdn_block_weights* w,
     hipLaunchKernelGGL(pack_kernel, dim3(b->steps, b->tb), dim3(64), 0, st, static_cast<const uint16_t*>(w->w_ba),
                        static_cast<const uint16_t*>(w->w_ba), out_ba, H, 0, 0, b->nb);
   }
+  if (b->fold)  // W_out [H, nv*dv] in the same 16-row tiles, after the b|a tiles
+    hipLaunchKernelGGL(pack_kernel, dim3(b->ko / 32, 4 * b->o), dim3(64), 0, st, static_cast<const uint16_t*>(w->w_out),
+                       static_cast<const uint16_t*>(w->w_out),
+                       reinterpret_cast<uint16_t*>(out + packed_qkvz_bytes(b) + packed_scale_bytes(b) + packed_ba_bytes(b)),
+                       b->ko, 4 * b->o, H, 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(b, GDN_E_HIP, std::string("gdn_block_pack_weights: ") + hipGetErrorString(e));
   return GDN_OK;
 }
 
-extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, const gdn_block_weights* w,
-                                void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
-                                void* core_out, void* stream) {
-  if (!b) return GDN_E_INVALID_ARG;
+namespace {
+int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_weights* w, void* conv_state,
+                void* ssm_state, const int32_t* state_idx, int32_t rows, void* core_out, void* out, void* stream) {
   const gdn_block_config& c = b->cfg;
   if (rows < 0 || rows > c.max_rows)
     return fail(b, GDN_E_INVALID_ARG,
                 "gdn_block_decode: rows must be in 0.." + std::to_string(c.max_rows) + " (got " +
                     std::to_string(rows) + ")");
   if (!w) return fail(b, GDN_E_INVALID_ARG, "gdn_block_decode: weights must not be NULL");
+  if (b->fold) {
+    if (!out || !aligned16(out))
+      return fail(b, GDN_E_INVALID_ARG, "gdn_block_decode_with_out_proj: out must be a 16-byte aligned pointer");
+    if (!w->w_proj_packed && (!w->w_out || !aligned16(w->w_out)))
+      return fail(b, GDN_E_INVALID_ARG, "gdn_block_decode_with_out_proj: w_out must be a 16-byte aligned pointer");
+  }
   const bool packed = w->w_proj_packed != nullptr;
   const bool normed = c.input_normed == 1;
   const void* scales = (b->mx && !packed) ? w->w_qkvz_scales : x;  // checked only when read
@@ -1334,6 +1480,14 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   a.dt_bias = static_cast<const uint16_t*>(w->dt_bias);
   a.gnw = static_cast<const uint16_t*>(w->gated_norm_w);
   a.core = static_cast<uint16_t*>(core_out);
+  a.fold = b->fold ? 1 : 0;
+  a.O = b->fold ? b->o : 0;
+  a.Ko = b->ko;
+  a.out = static_cast<uint16_t*>(out);
+  a.wo = static_cast<const uint16_t*>(w->w_out);
+  a.wo_pk = packed ? reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(w->w_proj_packed) +
+                                                       packed_qkvz_bytes(b) + packed_scale_bytes(b) + packed_ba_bytes(b))
+                   : nullptr;
   a.xn = b->xn;
   a.xq = b->xq;
   a.xqs = b->xqs;
@@ -1367,7 +1521,8 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   a.geps = c.gated_norm_eps;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int grid = rows * a.P + a.G + rows * c.num_v_heads;  // no norm workgroups with a normed input
+  // no norm workgroups with a normed input; the out_proj workgroups last
+  const int grid = rows * a.P + a.G + rows * c.num_v_heads + a.O;
   if (packed)
     launch<true>(b, a, grid, st);
   else
@@ -1375,6 +1530,27 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(b, GDN_E_HIP, std::string("gdn_block_decode: launch failed: ") + hipGetErrorString(e));
   return GDN_OK;
+}
+}  // namespace
+
+extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, const gdn_block_weights* w,
+                                void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
+                                void* core_out, void* stream) {
+  if (!b) return GDN_E_INVALID_ARG;
+  if (b->fold)
+    return fail(b, GDN_E_INVALID_ARG,
+                "gdn_block_decode: this handle folds out_proj; call gdn_block_decode_with_out_proj");
+  return decode_impl(b, x, residual, w, conv_state, ssm_state, state_idx, rows, core_out, nullptr, stream);
+}
+
+extern "C" int gdn_block_decode_with_out_proj(gdn_block_t b, const void* x, void* residual, const gdn_block_weights* w,
+                                              void* conv_state, void* ssm_state, const int32_t* state_idx,
+                                              int32_t rows, void* core_out, void* out, void* stream) {
+  if (!b) return GDN_E_INVALID_ARG;
+  if (!b->fold)
+    return fail(b, GDN_E_INVALID_ARG,
+                "gdn_block_decode_with_out_proj: this handle was created without fold_out_proj");
+  return decode_impl(b, x, residual, w, conv_state, ssm_state, state_idx, rows, core_out, out, stream);
 }
 
 extern "C" int gdn_block_check(gdn_block_t b, uint32_t* error_word) {

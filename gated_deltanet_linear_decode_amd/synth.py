@@ -5,7 +5,7 @@ method's arithmetic. The same bytes feed the HIP path and the CPU oracle.
 
 Distributions (the workloads of the pages carry random weights in the stock
 layouts, "sgl-amd-mono PR #89", Kernel checks):
-  bf16 weights (in_proj_qkvz, in_proj_ba, conv, both norm weights) ~ N(0, 0.02)
+  bf16 weights (in_proj_qkvz, in_proj_ba, conv, both norm weights, out_proj) ~ N(0, 0.02)
   A_log ~ U(0, 2) f32; dt_bias ~ N(0, 0.1) bf16
   x, residual ~ N(0, 1) bf16; conv state ~ N(0, 1) bf16
   SSM state ~ N(0, 0.1), stored f32 or bf16
@@ -40,6 +40,7 @@ class GdnWeights:
     A_log: torch.Tensor           # [nv] f32
     dt_bias: torch.Tensor         # [nv] bf16
     gated_norm_w: torch.Tensor    # [dv] bf16
+    w_out: torch.Tensor | None = None  # [H, nv*dv] bf16 out_proj (its rank's columns), fold only
 
     def tensors(self):
         return {k: v for k, v in self.__dict__.items() if v is not None}
@@ -81,7 +82,8 @@ def make_weights(shape: GdnShape, seed: int, *, gated_norm_stress: bool = False)
     dt_bias = _bf16(rng.normal(0.0, 0.1, s.num_v_heads))
     g = rng.normal(0.0, 0.02, s.head_v_dim)
     gated_norm_w = _bf16(1.0 + g if gated_norm_stress else g)
-    return GdnWeights(norm_w, w_qkvz, w_scales, w_ba, conv_w, A_log, dt_bias, gated_norm_w)
+    w_out = _bf16(rng.normal(0.0, 0.02, (H, s.value_dim))) if s.fold_out_proj else None
+    return GdnWeights(norm_w, w_qkvz, w_scales, w_ba, conv_w, A_log, dt_bias, gated_norm_w, w_out)
 
 
 def make_state_idx(shape: GdnShape, rows: int, seed: int, *, pads: bool | None = None,

@@ -108,6 +108,11 @@ typedef struct gdn_block_config {
                               norm) are skipped, residual and norm_w are neither read nor
                               written (they may be NULL), has_residual must be 0; with MXFP4
                               each projection workgroup quantises its K range of xn itself */
+  int32_t fold_out_proj;   /* 1: the launch also writes the rank's out_proj partial
+                              out = bf16(core W_out^T), [R, H] ("SGLang PR #43558",
+                              Modifications: K1 with out_proj folded in); needs nv*dv a
+                              multiple of 128 up to 1024; decode with
+                              gdn_block_decode_with_out_proj */
 } gdn_block_config;
 
 typedef struct gdn_block_weights {
@@ -120,6 +125,7 @@ typedef struct gdn_block_weights {
   const void* dt_bias;       /* [nv] bf16 */
   const void* gated_norm_w;  /* [dv] bf16 */
   const void* w_proj_packed; /* NULL, or the tiled copy from gdn_block_pack_weights */
+  const void* w_out;         /* [H, nv*dv] bf16 out_proj (this rank's K slice), fold only */
 } gdn_block_weights;
 
 typedef struct gdn_block* gdn_block_t;
@@ -148,14 +154,24 @@ int gdn_block_decode(gdn_block_t blk, const void* x, void* residual, const gdn_b
                      void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
                      void* core_out, void* stream);
 
+/* gdn_block_decode, plus the rank's out_proj partial: out [rows, H] bf16 (device,
+ * 16-byte aligned) = bf16(core_out W_out^T) with the sum in f32, one output row per
+ * input row (a pad row's partial is zero). Only for a handle created with
+ * fold_out_proj = 1 (gdn_block_decode refuses such a handle). */
+int gdn_block_decode_with_out_proj(gdn_block_t blk, const void* x, void* residual, const gdn_block_weights* w,
+                                   void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
+                                   void* core_out, void* out, void* stream);
+
 /* Size in bytes of the tiled projection copy (16-row tiles of [in_proj_qkvz;
  * in_proj_ba], the last b|a tile zero-padded): Nqkvz*H*2 (bf16) or Nqkvz*H/2 +
- * Nqkvz*H/32 (MXFP4), plus ceil(2*nv/16) * 16 * H * 2. 0 for a NULL handle. */
+ * Nqkvz*H/32 (MXFP4), plus ceil(2*nv/16) * 16 * H * 2, plus H * nv*dv * 2 with
+ * fold_out_proj (W_out in the same tiles). 0 for a NULL handle. */
 size_t gdn_block_packed_weight_bytes(gdn_block_t blk);
 
 /* Enqueue on `stream` the write of the tiled copy of w->w_qkvz (with w->w_qkvz_scales
- * for MXFP4) and w->w_ba, all row-major as above, into `packed` (device memory of
- * gdn_block_packed_weight_bytes bytes, 16-byte aligned, caller-owned). */
+ * for MXFP4), w->w_ba and, with fold_out_proj, w->w_out, all row-major as above, into
+ * `packed` (device memory of gdn_block_packed_weight_bytes bytes, 16-byte aligned,
+ * caller-owned). */
 int gdn_block_pack_weights(gdn_block_t blk, const gdn_block_weights* w, void* packed, void* stream);
 
 /* Quantise `rows` rows of `cols` bf16 values (x, [rows, cols], device, 16-byte aligned)

@@ -320,6 +320,15 @@ def gated_rmsnorm(o_bits, z_bits, w_bits, eps: float):
 # the whole block
 
 
+def out_proj(w_out_bits, core_bits):
+    """The rank's out_proj partial: out = bf16(core W_out^T), core [R, nv*dv] and W_out
+    [H, nv*dv] bf16, the sum exact in float64 and rounded once ("SGLang PR #43558",
+    Modifications: K1 with out_proj folded in writes the rank's out_proj partial; the
+    stock GEMM's output is bf16(fp32(exact sum)) there). A pad row's core is zero, so its
+    partial is zero."""
+    return project_bf16(w_out_bits, core_bits)
+
+
 def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, state_idx):
     """One decode step of the GDN block over R rows (inputs are not modified).
 
@@ -335,8 +344,11 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
     x, residual: [R, H] bf16 bits; conv_state [slots, W-1, Cd] bf16 bits;
     ssm_state [slots, nv, dk, dv] f32 or bf16 bits; state_idx [R] int32.
 
+    With weights["w_out"] ([H, nv*dv] bf16 bits) the rank's out_proj partial is
+    returned too (out [R, H] bf16 bits; else None).
+
     Returns dict(core [R, nv*dv] bf16 bits, residual [R, H] bf16 bits,
-                 conv_state, ssm_state (updated copies), y_qkvz, y_ba, xn).
+                 conv_state, ssm_state (updated copies), out, y_qkvz, y_ba, xn).
     """
     nk, dk = cfg["num_k_heads"], cfg["head_k_dim"]
     nv, dv = cfg["num_v_heads"], cfg["head_v_dim"]
@@ -384,5 +396,8 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
             core[row, hv * dv:(hv + 1) * dv] = gated_rmsnorm(
                 f64_to_bf16(o), z[hv], weights["gated_norm_w"], cfg["gated_norm_eps"])
 
-    return dict(core=core, residual=h, conv_state=conv_out, ssm_state=ssm_out,
+    out = None
+    if "w_out" in weights and weights["w_out"] is not None:
+        out = out_proj(weights["w_out"], core)
+    return dict(core=core, residual=h, conv_state=conv_out, ssm_state=ssm_out, out=out,
                 y_qkvz=y_qkvz, y_ba=y_ba, xn=xn)

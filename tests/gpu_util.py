@@ -43,11 +43,16 @@ def run_gpu(blk: GdnBlock, shape, wd: GdnWeights, cd: GdnCall, rows=None, packed
     conv = cd.conv_state.clone()
     ssm = cd.ssm_state.clone()
     core = torch.full((R, shape.value_dim), float("nan"), dtype=torch.bfloat16, device=cd.x.device)
+    out = (torch.full((R, shape.hidden), float("nan"), dtype=torch.bfloat16, device=cd.x.device)
+           if shape.fold_out_proj else None)
     ws = blk.packed_struct(wd, packed) if packed is not None else blk.weights_struct(wd)
-    blk.decode(cd.x, res, None, conv, ssm, cd.state_idx, core, weights_struct=ws)
+    blk.decode(cd.x, res, None, conv, ssm, cd.state_idx, core, weights_struct=ws, out=out)
     torch.cuda.synchronize()
     assert blk.check() == 0, "a wait inside the decode gave up"
-    return dict(core=core.cpu(), residual=res.cpu(), conv_state=conv.cpu(), ssm_state=ssm.cpu())
+    r = dict(core=core.cpu(), residual=res.cpu(), conv_state=conv.cpu(), ssm_state=ssm.cpu())
+    if out is not None:
+        r["out"] = out.cpu()
+    return r
 
 
 def same_bits(a: dict, b: dict):
@@ -114,6 +119,10 @@ def check_parity(shape, w, call, out, label="", flips=None):
     assert np.array_equal(conv_g[untouched], u16(call.conv_state)[untouched]), f"{label}: untouched conv slot changed"
     assert np.array_equal(ssm_g[untouched], oracle_state(call.ssm_state)[untouched]), \
         f"{label}: untouched ssm slot changed"
+    if shape.fold_out_proj:  # the out_proj partial: pad rows are zero
+        og_ = u16(out["out"])
+        assert np.all((og_[~valid] & 0x7FFF) == 0), f"{label}: pad row out_proj partial not zero"
+        stats["out"] = close(f"{label} out_proj", og_[valid], ref["out"][valid], flips=flips)
     if len(slots):
         stats["conv"] = close(f"{label} conv_state", conv_g[slots], conv_r[slots], flips=flips)
         stats["ssm"] = close(f"{label} ssm_state", ssm_g[slots], ssm_r[slots], bf16=bf16_state, flips=flips)

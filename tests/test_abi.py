@@ -75,6 +75,12 @@ def test_normed_input_refuses_a_residual_input():
     assert e.value.code == abi.GDN_E_UNSUPPORTED and "input_normed" in str(e.value)
 
 
+def test_out_proj_fold_needs_one_k_range():
+    with pytest.raises(abi.GdnError) as e:
+        abi.gdn_block_create(_cfg(fold_out_proj=1, num_v_heads=64, head_v_dim=32, head_k_dim=32))
+    assert e.value.code == abi.GDN_E_UNSUPPORTED and "fold_out_proj" in str(e.value)
+
+
 def test_create_lists_every_reason():
     with pytest.raises(abi.GdnError) as e:
         abi.gdn_block_create(_cfg(hidden=100, conv_width=5, max_rows=40, has_residual=3))

@@ -78,3 +78,21 @@ def test_tiny_normed_input(rows):
 @pytest.mark.parametrize("rows", [1, 5, 16])
 def test_tp8_rank_normed_input(rows):
     _case(configs.TP8_RANK_BF16_NORMED.with_(pad_rows=True), rows, 41)
+
+
+@pytest.mark.parametrize("rows", [1, 7, 16])
+def test_tiny_out_proj_fold(rows):
+    """The rank's out_proj partial written by the same launch ("SGLang PR #43558",
+    Modifications: K1 with the out_proj fold)."""
+    shape = configs.TINY.with_(name="tiny_out_proj", fold_out_proj=True, num_state_slots=24, pad_rows=True,
+                               rows=(16,))
+    _case(shape, rows, 500 + rows)
+
+
+@pytest.mark.parametrize("rows", [1, 8, 16])
+def test_tp8_rank_out_proj_fold(rows):
+    _case(configs.TP8_RANK_BF16_OUT.with_(pad_rows=True), rows, 61)
+
+
+def test_tp8_rank_mxfp4_normed_out_proj_fold():
+    _case(configs.TP8_RANK_MXFP4_NORMED.with_(fold_out_proj=True), 9, 62)

@@ -22,7 +22,7 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tp8_rank_f32_state_pads", "tp8_rank_mxfp4",
-                                  "tp8_rank_mxfp4_normed_input"])
+                                  "tp8_rank_mxfp4_normed_input", "tp8_rank_bf16_state_out_proj"])
 def test_batch_invariance(name):
     """A probe row's outputs do not change with the other rows or the width."""
     shape = configs.ALL[name].with_(num_state_slots=40, rows=(16,), pad_rows=False)
@@ -43,7 +43,7 @@ def test_batch_invariance(name):
             call = synth.GdnCall(x, res, base.conv_state, base.ssm_state, idx)
             out = run_gpu(blk, shape, w, call_to(call, DEV))
             got = (u16(out["core"][pos]), u16(out["residual"][pos]), u16(out["conv_state"][probe_slot]),
-                   _bits(out["ssm_state"][probe_slot]))
+                   _bits(out["ssm_state"][probe_slot])) + ((u16(out["out"][pos]),) if "out" in out else ())
             if ref is None:
                 ref = got
             for a, b in zip(ref, got):
