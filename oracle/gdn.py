@@ -220,6 +220,88 @@ def project_mxfp4(w_packed, w_scales, xn_bits):
     return f64_to_bf16(xq @ w.T)
 
 
+# MXFP6 E2M3 weights with bf16 activations (W6A16): "vLLM PR #60833", a reviewer's
+# comment proposing MXFP6 for the GDN projections (how to make the weights, and their
+# packing for the kernels).
+#
+# OCP E2M3: a 6-bit code sign | 2 exponent bits | 3 mantissa bits, exponent bias 1; a zero
+# exponent field is subnormal (m / 8), otherwise (1 + m / 8) * 2^(exp - 1); the largest
+# magnitude is 7.5. One e8m0 byte scales each block of 32 along K by 2^(byte - 127).
+
+E2M3_VALUES = np.array([m / 8.0 for m in range(8)] +
+                       [(1.0 + m / 8.0) * 2.0 ** (e - 1) for e in range(1, 4) for m in range(8)])
+
+
+def mxfp6_round(v):
+    """The pages' rounding of weights onto MXFP6 E2M3, one block of 32 along K at a time.
+
+    The block scale follows the MXFP4 RCEIL scheme with the E2M3 maximum 7.5: the block
+    maximum is rounded to 3 mantissa bits (half up, a carry moving into the exponent), and
+    with E the exponent of that rounded maximum the scale is 2^(E - 2), clamped to
+    2^[-126, 127] (an all-zero block keeps 2^-126, a normal scale). Each |v| / scale is
+    rounded to the nearest E2M3 magnitude, ties to the even code (steps of 1/8 below 2,
+    1/4 below 4, 1/2 above), saturating at 7.5. A zero code carries no sign.
+
+    Returns (codes uint8 [..., K] with the sign at bit 5, scale bytes uint8 [..., K/32]).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    blocks = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
+    amax = np.abs(blocks).max(axis=-1)
+    mant, ex = np.frexp(amax)                    # amax = mant * 2^ex, mant in [0.5, 1)
+    E = (ex - 1).astype(np.int64)                # amax = (2 mant) 2^E, 2 mant in [1, 2)
+    E = E + (2.0 * mant >= 1.9375)               # 1.111 1b and above round up to 2
+    e = np.where(amax > 0, E - 2, -126)
+    e = np.clip(e, -126, 127)
+    a = np.abs(blocks) / np.exp2(e.astype(np.float64))[..., None]
+    step = np.where(a < 2.0, 0.125, np.where(a < 4.0, 0.25, 0.5))
+    q = np.minimum(np.round(a / step) * step, 7.5)       # np.round: half to even
+    mag = np.searchsorted(E2M3_VALUES, q)
+    assert np.all(E2M3_VALUES[mag] == q)
+    sign = (blocks < 0) & (mag > 0)
+    codes = (mag | (sign.astype(np.int64) << 5)).astype(np.uint8)
+    return codes.reshape(v.shape), (e + 127).astype(np.uint8)
+
+
+def mxfp6_dequantize(codes, scale_bytes):
+    """Values of E2M3 codes (uint8 [..., K]) with e8m0 block scales ([..., K/32])."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    mag = E2M3_VALUES[codes & 31]
+    val = np.where(codes & 32, -mag, mag)
+    sc = np.exp2(np.asarray(scale_bytes, dtype=np.float64) - 127.0)
+    return val * np.repeat(sc, 32, axis=-1)
+
+
+def pack_e2m3(codes):
+    """[..., K] codes -> [..., K/32, 24] bytes: code i of a block at bits 6i .. 6i+5 of
+    the block's 24 bytes read as one little-endian 192-bit number."""
+    c = np.asarray(codes, dtype=np.uint8)
+    blk = c.reshape(c.shape[:-1] + (c.shape[-1] // 32, 32)).astype(np.uint64)
+    out = np.zeros(blk.shape[:-1] + (24,), dtype=np.uint8)
+    for i in range(32):
+        for b in range(6):
+            bit = 6 * i + b
+            out[..., bit // 8] |= (((blk[..., i] >> np.uint64(b)) & np.uint64(1)) << np.uint64(bit % 8)).astype(np.uint8)
+    return out
+
+
+def unpack_e2m3(packed):
+    """[..., K/32, 24] bytes (or [..., K*3/4]) -> [..., K] codes (inverse of pack_e2m3)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    p = p.reshape(p.shape[:-1] + (p.shape[-1] // 24, 24)) if p.shape[-1] != 24 else p
+    bits = np.unpackbits(p, axis=-1, bitorder="little")          # [..., nb, 192]
+    bits = bits.reshape(bits.shape[:-1] + (32, 6)).astype(np.uint8)
+    codes = (bits * (1 << np.arange(6, dtype=np.uint8))).sum(axis=-1).astype(np.uint8)
+    return codes.reshape(codes.shape[:-2] + (codes.shape[-2] * 32,))
+
+
+def project_mxfp6(w_packed, w_scales, xn_bits):
+    """y = bf16(sum over K of dequant(W) * xn) for MXFP6 E2M3 weights and bf16 activations
+    (W6A16: the activations are not quantised). An E2M3 value times a power of two is a
+    bf16 value, and the sum is exact in float64 before the one rounding."""
+    w = mxfp6_dequantize(unpack_e2m3(w_packed), w_scales)
+    return f64_to_bf16(bf16_to_f64(xn_bits) @ w.T)
+
+
 # --------------------------------------------------------------------------------------
 # step 4: split of the projection outputs (the stock chain's separate split kernel,
 # "sgl-amd-mono PR #89", Kernels before and after). Grouped per key head:
@@ -334,13 +416,13 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
 
     cfg: hidden, num_k_heads, head_k_dim, num_v_heads, head_v_dim, conv_width,
          ssm_state_dtype ('f32'|'bf16'), has_residual, qkvz_format
-         ('bf16'|'mxfp4'), norm_eps, gated_norm_eps, l2norm_eps, and optionally
+         ('bf16'|'mxfp4'|'mxfp6'), norm_eps, gated_norm_eps, l2norm_eps, and optionally
          input_normed: x is already the norm's output xn ("SGLang PR #43558",
          Modifications: the "normed" K1 build starts from input_layernorm's
          output), so the residual add and the norm are skipped and the
          residual is neither read nor returned (None).
-    weights: norm_w, w_qkvz (bf16 bits [Nqkvz, H] or packed e2m1 [Nqkvz, H/2]),
-         w_qkvz_scales (MXFP4 only), w_ba, conv_w, A_log (f32), dt_bias, gated_norm_w.
+    weights: norm_w, w_qkvz (bf16 bits [Nqkvz, H], packed e2m1 [Nqkvz, H/2] or packed
+         E2M3 [Nqkvz, H/32, 24]), w_qkvz_scales (MXFP4 and MXFP6 only), w_ba, conv_w, A_log (f32), dt_bias, gated_norm_w.
     x, residual: [R, H] bf16 bits; conv_state [slots, W-1, Cd] bf16 bits;
     ssm_state [slots, nv, dk, dv] f32 or bf16 bits; state_idx [R] int32.
 
@@ -363,6 +445,8 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
         xn = gemma_rmsnorm(h, weights["norm_w"], cfg["norm_eps"])
     if cfg["qkvz_format"] == "mxfp4":
         y_qkvz = project_mxfp4(weights["w_qkvz"], weights["w_qkvz_scales"], xn)
+    elif cfg["qkvz_format"] == "mxfp6":
+        y_qkvz = project_mxfp6(weights["w_qkvz"], weights["w_qkvz_scales"], xn)
     else:
         y_qkvz = project_bf16(weights["w_qkvz"], xn)
     y_ba = project_bf16(weights["w_ba"], xn)
