@@ -193,6 +193,90 @@ def test_mxfp4_projection_exact_against_integer_arithmetic():
     assert np.array_equal(got, og.bf16_to_f64(og.f64_to_bf16(exact)))
 
 
+def test_e2m3_table_ocp_facts():
+    """OCP E2M3: largest magnitude 7.5 (code 0x1F), smallest subnormal 1/8 (0x01), smallest
+    normal 1 (0x08), steps 1/8 below 2, 1/4 below 4, 1/2 up to 7.5, sign at bit 5."""
+    t = og.E2M3_VALUES
+    assert len(t) == 32 and t[0x1F] == 7.5 and t[0x01] == 0.125 and t[0x08] == 1.0
+    assert np.all(np.diff(t) > 0)
+    assert np.all(np.diff(t[:17]) == 0.125) and np.all(np.diff(t[16:25]) == 0.25) and np.all(np.diff(t[24:]) == 0.5)
+    v = og.mxfp6_dequantize(np.array([0x21, 0x3F, 0x20, 0x08], np.uint8).repeat(8), np.array([127], np.uint8))
+    assert v[0] == -0.125 and v[8] == -7.5 and v[16] == 0.0 and v[24] == 1.0
+
+
+def test_mxfp6_hand_worked_blocks():
+    fx = _golden("mxfp6_blocks.json")
+    for blk in fx["blocks"]:
+        v = np.zeros(32)
+        for i, val in blk["values"].items():
+            v[int(i)] = float.fromhex(val) if isinstance(val, str) else val
+        codes, scales = og.mxfp6_round(v)
+        assert int(scales[0]) == blk["scale_byte"], blk["note"]
+        want = np.zeros(32, dtype=np.uint8)
+        for i, c in blk["codes"].items():
+            want[int(i)] = c
+        assert np.array_equal(codes, want), blk["note"]
+
+
+def test_mxfp6_round_trip_on_representable_blocks():
+    """A block whose largest magnitude lies in the top binade (4 .. 7.5 times its scale)
+    rounds back to itself: the scale is recovered and every value is on the grid."""
+    rng = np.random.default_rng(16)
+    codes = rng.integers(0, 64, (6, 96)).astype(np.uint8)
+    codes[:, [0, 32, 64]] = rng.integers(24, 32, (6, 3))    # a top-binade maximum per block
+    codes[:, 1:32] &= 0x37                                   # the others at most 3.75 ... 7.5
+    codes[codes == 0x20] = 0                                 # -0 rounds to +0
+    scales = rng.integers(100, 140, (6, 3)).astype(np.uint8)
+    v = og.mxfp6_dequantize(codes, scales)
+    c2, s2 = og.mxfp6_round(v)
+    assert np.array_equal(s2, scales) and np.array_equal(c2, codes)
+
+
+def test_e2m3_packing_bit_positions():
+    """Code i of a block sits at bits 6i .. 6i+5 of its 24 bytes, little-endian."""
+    c = np.zeros(32, np.uint8)
+    c[0] = 1
+    assert og.pack_e2m3(c)[0].tolist() == [1] + [0] * 23
+    c[:] = 0
+    c[1] = 1                       # bit 6
+    assert og.pack_e2m3(c)[0].tolist() == [0x40] + [0] * 23
+    c[:] = 0
+    c[31] = 63                     # bits 186 .. 191: the top 6 bits of byte 23
+    assert og.pack_e2m3(c)[0].tolist() == [0] * 23 + [0xFC]
+    c[:] = 0
+    c[4] = 0x2B                    # bits 24 .. 29: byte 3 = 0x2B
+    c[5] = 0x15                    # bits 30 .. 35: 0b010101 -> byte 3 bits 6,7 = 01, byte 4 = 0101
+    p = og.pack_e2m3(c)[0]
+    assert p[3] == (0x2B | (0x1 << 6)) and p[4] == 0x5
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 64, (4, 128)).astype(np.uint8)
+    assert np.array_equal(og.unpack_e2m3(og.pack_e2m3(codes)), codes)
+
+
+def test_mxfp6_projection_exact_against_integer_arithmetic():
+    """E2M3 values are multiples of 1/8: with scale 2^0 and small integer activations the
+    projection is an integer sum divided by 8, rounded once."""
+    rng = np.random.default_rng(17)
+    N, H = 5, 96
+    wcodes = rng.integers(0, 64, (N, H)).astype(np.uint8)
+    wscales = np.full((N, H // 32), 127, dtype=np.uint8)
+    xi = rng.integers(-8, 9, (3, H))
+    xb = og.f64_to_bf16(xi.astype(np.float64))
+    got = og.bf16_to_f64(og.project_mxfp6(og.pack_e2m3(wcodes), wscales, xb))
+    mag8 = np.array([m for m in range(8)] + [(8 + m) << (e - 1) for e in range(1, 4) for m in range(8)])
+    wi = np.where(wcodes & 32, -1, 1) * mag8[wcodes & 31]
+    exact = (xi @ wi.T) / 8.0
+    assert np.array_equal(got, og.bf16_to_f64(og.f64_to_bf16(exact)))
+    # a scale byte b multiplies by 2^(b - 127), per block of 32
+    ws2 = wscales.copy()
+    ws2[:, 1] = 130
+    got2 = og.bf16_to_f64(og.project_mxfp6(og.pack_e2m3(wcodes), ws2, xb))
+    f = np.ones(H)
+    f[32:64] = 8.0
+    exact2 = (xi @ (wi * f).T) / 8.0
+    assert np.array_equal(got2, og.bf16_to_f64(og.f64_to_bf16(exact2)))
+
+
 # ----------------------------------------------------------------------------------------
 # split
 
