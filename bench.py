@@ -197,7 +197,7 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=960)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workloads", default="tp8_rank_f32_state_pads,dense_full_width,tp8_rank_mxfp4,"
+    ap.add_argument("--workloads", default="tp8_rank_f32_state_pads,dense_full_width,tp8_rank_mxfp4,tp8_rank_mxfp6,"
                     "tp8_rank_bf16_state_normed_input,tp8_rank_mxfp4_normed_input,tp8_rank_bf16_state_out_proj",
                     help="other workloads to sweep (tiled weights) after the headline; '' for none")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -17,13 +17,14 @@ GDN_E_UNSUPPORTED = -2
 GDN_E_HIP = -3
 GDN_FMT_BF16 = 0
 GDN_FMT_MXFP4 = 1
+GDN_FMT_MXFP6 = 2
 GDN_STATE_F32 = 0
 GDN_STATE_BF16 = 1
 GDN_MAX_ROWS = 16
 
 EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error",
             "gdn_block_packed_weight_bytes", "gdn_block_pack_weights", "gdn_block_check",
-            "gdn_mxfp4_quantize", "gdn_block_decode_with_out_proj")
+            "gdn_mxfp4_quantize", "gdn_block_decode_with_out_proj", "gdn_mxfp6_round_weights")
 
 
 class GdnBlockConfig(ctypes.Structure):
@@ -85,6 +86,8 @@ def load() -> ctypes.CDLL:
         lib.gdn_block_decode_with_out_proj.restype = c_int
         lib.gdn_mxfp4_quantize.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
         lib.gdn_mxfp4_quantize.restype = c_int
+        lib.gdn_mxfp6_round_weights.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
+        lib.gdn_mxfp6_round_weights.restype = c_int
         _lib = lib
     return _lib
 
@@ -139,6 +142,12 @@ def gdn_block_check(handle) -> int:
 
 def gdn_mxfp4_quantize(x: int, rows: int, cols: int, codes: int, scales: int, stream: int) -> None:
     rc = load().gdn_mxfp4_quantize(x, rows, cols, codes, scales, stream)
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(None))
+
+
+def gdn_mxfp6_round_weights(w: int, rows: int, cols: int, codes: int, scales: int, stream: int) -> None:
+    rc = load().gdn_mxfp6_round_weights(w, rows, cols, codes, scales, stream)
     if rc != GDN_OK:
         raise GdnError(rc, gdn_block_last_error(None))
 

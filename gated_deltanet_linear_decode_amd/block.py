@@ -8,7 +8,9 @@ from __future__ import annotations
 import torch
 
 from . import abi
-from .configs import FMT_MXFP4, SSM_BF16, GdnShape
+from .configs import FMT_MXFP4, FMT_MXFP6, SSM_BF16, GdnShape
+
+_FMT = {FMT_MXFP4: abi.GDN_FMT_MXFP4, FMT_MXFP6: abi.GDN_FMT_MXFP6}
 
 
 def make_config(shape: GdnShape, max_rows: int | None = None) -> abi.GdnBlockConfig:
@@ -17,7 +19,7 @@ def make_config(shape: GdnShape, max_rows: int | None = None) -> abi.GdnBlockCon
         hidden=s.hidden, num_k_heads=s.num_k_heads, head_k_dim=s.head_k_dim,
         num_v_heads=s.num_v_heads, head_v_dim=s.head_v_dim, conv_width=s.conv_width,
         num_state_slots=s.num_state_slots, max_rows=s.max_rows if max_rows is None else max_rows,
-        qkvz_format=abi.GDN_FMT_MXFP4 if s.qkvz_format == FMT_MXFP4 else abi.GDN_FMT_BF16,
+        qkvz_format=_FMT.get(s.qkvz_format, abi.GDN_FMT_BF16),
         ssm_state_dtype=abi.GDN_STATE_BF16 if s.ssm_state_dtype == SSM_BF16 else abi.GDN_STATE_F32,
         has_residual=1 if s.has_residual else 0,
         norm_eps=s.norm_eps, gated_norm_eps=s.gated_norm_eps, l2norm_eps=s.l2norm_eps,
@@ -67,6 +69,9 @@ class GdnBlock:
         st.norm_w = None if s.input_normed else _check(w.norm_w, "norm_w", torch.bfloat16, (H,), d)
         if s.qkvz_format == FMT_MXFP4:
             st.w_qkvz = _check(w.w_qkvz, "w_qkvz", torch.uint8, (s.n_qkvz, H // 2), d)
+            st.w_qkvz_scales = _check(w.w_qkvz_scales, "w_qkvz_scales", torch.uint8, (s.n_qkvz, H // 32), d)
+        elif s.qkvz_format == FMT_MXFP6:
+            st.w_qkvz = _check(w.w_qkvz, "w_qkvz", torch.uint8, (s.n_qkvz, H // 32, 24), d)
             st.w_qkvz_scales = _check(w.w_qkvz_scales, "w_qkvz_scales", torch.uint8, (s.n_qkvz, H // 32), d)
         else:
             st.w_qkvz = _check(w.w_qkvz, "w_qkvz", torch.bfloat16, (s.n_qkvz, H), d)

@@ -9,7 +9,9 @@ The shapes follow the pages:
   * "vLLM PR #60833" (Per launch table): the same share with an MXFP4
     in_proj_qkvz, timed at 1 to 16 rows with weights rotated past the MALL;
   * "SGLang PR #43558" (Modifications, K1 at TP1): the full-width dense layer,
-    hidden 5120 with 16 key and 48 value heads of 128.
+    hidden 5120 with 16 key and 48 value heads of 128;
+  * "vLLM PR #60833" (a reviewer's comment proposing MXFP6): the TP8 share with
+    an MXFP6 E2M3 in_proj_qkvz read by K1 with bf16 activations, timed at 2 rows.
 """
 from __future__ import annotations
 
@@ -19,6 +21,7 @@ SSM_F32 = "f32"
 SSM_BF16 = "bf16"
 FMT_BF16 = "bf16"
 FMT_MXFP4 = "mxfp4"
+FMT_MXFP6 = "mxfp6"
 
 
 @dataclass(frozen=True)
@@ -122,6 +125,12 @@ TP8_RANK_MXFP4 = GdnShape(
     description="one TP8 rank's share, MXFP4 in_proj_qkvz, bf16 state, pad rows",
 )
 
+# MXFP6 E2M3 in_proj_qkvz with bf16 activations; 19.7 MB of weights a layer, so 32 layer
+# copies (630 MB) keep the MALL from holding a layer between its launches
+TP8_RANK_MXFP6 = TP8_RANK_MXFP4.with_(
+    name="tp8_rank_mxfp6", qkvz_format=FMT_MXFP6, layers=32,
+    description="one TP8 rank's share, MXFP6 E2M3 in_proj_qkvz (W6A16), bf16 state, pad rows")
+
 # the "normed" variant: the block starts from the norm's output ("SGLang PR #43558",
 # Modifications: K1Build.normed)
 TP8_RANK_BF16_NORMED = TP8_RANK_BF16.with_(
@@ -138,7 +147,7 @@ TP8_RANK_BF16_OUT = TP8_RANK_BF16.with_(
     description="one TP8 rank's share, bf16 state, out_proj partial folded in")
 
 ALL = {s.name: s for s in (TINY, TP8_RANK_BF16, TP8_RANK_F32, DENSE_FULL, TP8_RANK_MXFP4,
-                           TP8_RANK_BF16_NORMED, TP8_RANK_MXFP4_NORMED, TP8_RANK_BF16_OUT)}
+                           TP8_RANK_MXFP6, TP8_RANK_BF16_NORMED, TP8_RANK_MXFP4_NORMED, TP8_RANK_BF16_OUT)}
 
 
 def algorithmic_bytes(shape: GdnShape, rows: int, valid_rows: int | None = None) -> int:
@@ -153,6 +162,8 @@ def algorithmic_bytes(shape: GdnShape, rows: int, valid_rows: int | None = None)
     H = s.hidden
     if s.qkvz_format == FMT_MXFP4:
         w_qkvz = H * s.n_qkvz // 2 + H * s.n_qkvz // 32
+    elif s.qkvz_format == FMT_MXFP6:
+        w_qkvz = H * s.n_qkvz * 3 // 4 + H * s.n_qkvz // 32
     else:
         w_qkvz = 2 * H * s.n_qkvz
     w_other = 2 * H * s.n_ba + 2 * H + 2 * s.conv_dim * s.conv_width + 4 * s.num_v_heads \

@@ -63,6 +63,12 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+typedef __attribute__((ext_vector_type(6))) unsigned u32x6_t;
+typedef __attribute__((ext_vector_type(32))) __bf16 bf16x32_t;
+
+// in_proj_qkvz formats (the values of GDN_FMT_*)
+constexpr int kFmtBf16 = 0, kFmtMx4 = 1, kFmtMx6 = 2;
 
 constexpr int kConvW = 4;          // conv width; create() refuses any other
 constexpr int kThreads = 256;      // every role runs 4 waves of 64
@@ -696,14 +702,113 @@ __device__ void proj_mx(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   TRACE_HWID(7);
 }
 
+// MXFP6 E2M3 in_proj_qkvz with bf16 activations (W6A16, "vLLM PR #60833", a reviewer's
+// comment proposing MXFP6 for the GDN projections: one v_cvt_scalef32_pk32_bf16_fp6 turns
+// a lane's 32 codes times their block scale into 32 bf16 values exactly, and those feed
+// the bf16 matrix cores with the bf16 activations). In a unit of 128 K, lane l holds the
+// 32 codes of row l % 16 at k = 128 U + 32 (l / 16) (24 bytes, one e8m0 scale); converted,
+// its 4 runs of 8 bf16 are the A operands of 4 MFMAs whose B operands are the activations
+// at k = 128 U + 32 (l / 16) + 8 i, so within a unit the K order differs from the bf16
+// tiles' in the same way for both operands. A wave streams tile t0 + wave over the K
+// range in groups of 4 units (one scale dword per lane and group) and keeps every group
+// of the range in flight.
+constexpr int kGrp6 = kKr / 512;  // groups of 4 units in a K range at most
+
+struct Mx6Group {
+  u32x4_t lo[4];  // the first 16 code bytes of each unit
+  u32x2_t hi[4];  // the last 8
+  uint32_t sc;    // byte u: the scale of unit u
+};
+
+template <bool PACKED>
+__device__ __forceinline__ void mx6_wload(const Args& a, int t, int G, int lane, Mx6Group& m) {
+  if (PACKED) {
+    // a unit is 1.5 KiB: the 64 lanes' 16-byte parts, then their 8-byte parts
+    const uint8_t* u0 = reinterpret_cast<const uint8_t*>(a.wpk) + ((size_t)t * (a.H >> 7) + 4 * G) * 1536;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      m.lo[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(u0 + u * 1536 + 16 * lane));
+      m.hi[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(u0 + u * 1536 + 1024 + 8 * lane));
+    }
+    m.sc = __builtin_nontemporal_load(a.wpk_sc + ((size_t)t * (a.H >> 9) + G) * 64 + lane);
+  } else {
+    // row-major codes [Nq, H/32, 24]: block 16 G + 4 u + kb of the row is unit u's
+    const int row = t * 16 + (lane & 15), kb = lane >> 4;
+    const uint8_t* c = a.wqc + ((size_t)row * (a.H >> 5) + 16 * G + kb) * 24;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x2_t p0 = *reinterpret_cast<const u32x2_t*>(c + 96 * u);
+      const u32x2_t p1 = *reinterpret_cast<const u32x2_t*>(c + 96 * u + 8);
+      m.lo[u] = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
+      m.hi[u] = *reinterpret_cast<const u32x2_t*>(c + 96 * u + 16);
+    }
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(a.wqs + (size_t)row * (a.H >> 5) + 16 * G);
+    m.sc = ((q[0] >> (8 * kb)) & 0xffu) | (((q[1] >> (8 * kb)) & 0xffu) << 8) |
+           (((q[2] >> (8 * kb)) & 0xffu) << 16) | (((q[3] >> (8 * kb)) & 0xffu) << 24);
+  }
+}
+
+template <bool PACKED>
+__device__ void proj_mx6(const Args& a, int gb, int t0, int s, ProjShared& sh) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, kb = lane >> 4;
+  const int t = t0 + wave;
+  const int ng = a.Kr >> 9, g0 = s * ng;  // groups in the range; first global group
+  const int rot = (t * 7 + s * 3) % ng;   // spread concurrent streams over the channels
+  auto lgrp = [&](int m) { return m + rot < ng ? m + rot : m + rot - ng; };
+  XnIn xi;
+  if (a.normed) xin_issue(a, s * a.Kr, xi);
+  Mx6Group w[kGrp6];
+#pragma unroll
+  for (int m = 0; m < kGrp6; ++m)
+    if (m < ng) mx6_wload<PACKED>(a, t, g0 + lgrp(m), lane, w[m]);
+
+  if (a.normed)
+    xin_store(a, xi, sh);
+  else
+    stage_xn(a, gb, s * a.Kr, sh);
+  const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int m = 0; m < kGrp6; ++m) {
+    if (m < ng) {
+      const int gl = lgrp(m);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        // the scale operand's exponent field is the e8m0 byte: the conversion multiplies by
+        // 2^(byte - 127) exactly
+        const float scale = __uint_as_float(((w[m].sc >> (8 * u)) & 0xffu) << 23);
+        const u32x6_t src = {w[m].lo[u][0], w[m].lo[u][1], w[m].lo[u][2], w[m].lo[u][3], w[m].hi[u][0], w[m].hi[u][1]};
+        const bf16x32_t v = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(src, scale);
+        const uint16_t* xk = &sh.xs[xrow][128 * (4 * gl + u) + 32 * kb];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(v, v, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                      as_bf16x8(*reinterpret_cast<const u32x4_t*>(xk)), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(v, v, 8, 9, 10, 11, 12, 13, 14, 15),
+                                                      as_bf16x8(*reinterpret_cast<const u32x4_t*>(xk + 8)), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_shufflevector(v, v, 16, 17, 18, 19, 20, 21, 22, 23),
+            as_bf16x8(*reinterpret_cast<const u32x4_t*>(xk + 16)), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_shufflevector(v, v, 24, 25, 26, 27, 28, 29, 30, 31),
+            as_bf16x8(*reinterpret_cast<const u32x4_t*>(xk + 24)), acc, 0, 0, 0);
+      }
+    }
+  }
+  TRACE_POINT(2);
+  publish_tiles(a, t0, s, acc);
+  TRACE_POINT(3);
+  TRACE_HWID(7);
+}
+
 // projection workgroup gb: groups of 4 in_proj_qkvz tiles first, then the b|a tiles; S K
 // ranges each
-template <bool PACKED, bool MX>
+template <bool PACKED, int FMT>
 __device__ void proj_role(const Args& a, int gb, ProjShared& sh) {
   if (gb < a.Gq) {
     const int tg = gb / a.S, s = gb - tg * a.S;
-    if (MX)
+    if (FMT == kFmtMx4)
       proj_mx<PACKED>(a, gb, 4 * tg, s, sh);
+    else if (FMT == kFmtMx6)
+      proj_mx6<PACKED>(a, gb, 4 * tg, s, sh);
     else
       proj_bf16<PACKED, true>(a, gb, 4 * tg, s, sh);
   } else {
@@ -1109,7 +1214,7 @@ __device__ void oproj_role(const Args& a, int ob, ProjShared& sh) {
 
 // FOLD is a template flag, not only a launch argument, so that the out_proj role's register
 // tile does not raise the register count (and lower the occupancy) of the launches without it.
-template <bool PACKED, bool MX, int DK, typename ST, bool FOLD>
+template <bool PACKED, int FMT, int DK, typename ST, bool FOLD>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   __shared__ union {
     ProjShared proj;
@@ -1119,9 +1224,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   TRACE_POINT(0);
   const int nn = a.R * a.P, nr = a.R * a.nv;
   if (b < nn) {
-    norm_role<MX>(a, b, sh.rec.bsum);
+    norm_role<FMT == kFmtMx4>(a, b, sh.rec.bsum);
   } else if (b < nn + a.G) {
-    proj_role<PACKED, MX>(a, b - nn, sh.proj);
+    proj_role<PACKED, FMT>(a, b - nn, sh.proj);
   } else if (b < nn + a.G + nr) {
     rec_role<DK, ST>(a, b - nn - a.G, sh.rec);
   } else if (FOLD) {
@@ -1163,6 +1268,70 @@ __global__ __launch_bounds__(64) void pack_mx_scales_kernel(const uint8_t* __res
   out[((size_t)t * (H >> 9) + U) * 64 + l] = d;
 }
 
+// tiled copy of MXFP6 in_proj_qkvz codes: unit (t, U) = 1.5 KiB, the 16-byte heads of the 64
+// lanes' code runs, then their 8-byte tails; lane l holding the 32 codes (24 bytes) of row
+// 16 t + l % 16 at k = 128 U + 32 (l / 16). The scales take the MXFP4 scale tiles' layout.
+__global__ __launch_bounds__(64) void pack_mx6_codes_kernel(const uint8_t* __restrict__ wq, uint8_t* __restrict__ out,
+                                                            int H) {
+  const int U = blockIdx.x, t = blockIdx.y, l = threadIdx.x, row = t * 16 + (l & 15);
+  const uint8_t* src = wq + ((size_t)row * (H >> 5) + 4 * U + (l >> 4)) * 24;
+  const u32x2_t p0 = *reinterpret_cast<const u32x2_t*>(src), p1 = *reinterpret_cast<const u32x2_t*>(src + 8);
+  const u32x2_t p2 = *reinterpret_cast<const u32x2_t*>(src + 16);
+  uint8_t* dst = out + ((size_t)t * (H >> 7) + U) * 1536;
+  *reinterpret_cast<u32x4_t*>(dst + 16 * l) = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
+  *reinterpret_cast<u32x2_t*>(dst + 1024 + 8 * l) = p2;
+}
+
+// bf16 weights -> MXFP6 E2M3 blocks of 32 ("vLLM PR #60833", a reviewer's comment proposing
+// MXFP6, step 2): one thread per block. The block maximum rounded to 3 mantissa bits
+// carries into the next binade exactly when its top 4 mantissa bits are all set, which for
+// a bf16 maximum is bits 6..3 of its 7; the scale exponent is that binade's minus 2, clamped
+// to [-126, 127]. Each |x| / 2^e (exact) is rounded to the nearest E2M3 magnitude with ties
+// to the even code: rint of |x| / 2^e at the step of its binade (1/8 below 2, 1/4 below 4,
+// 1/2 above) counts grid points, and the code follows from the count (n for steps of 1/8,
+// n + 8 for 1/4, n + 16 for 1/2, as E2M3 codes grow by one per grid point). A zero code
+// carries no sign. Codes go out packed, code i at bits 6i..6i+5 of the block's 24 bytes.
+__global__ __launch_bounds__(kThreads) void mx6_round_kernel(const uint16_t* __restrict__ w, uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales, long long nblk) {
+  const long long b = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (b >= nblk) return;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(w + b * 32);
+  uint32_t v[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4_t t = src[q];
+    v[4 * q] = t[0];
+    v[4 * q + 1] = t[1];
+    v[4 * q + 2] = t[2];
+    v[4 * q + 3] = t[3];
+  }
+  uint32_t m = 0;  // the largest magnitude, as bf16 bits (finite values order like their bits)
+#pragma unroll
+  for (int q = 0; q < 16; ++q) m = max(m, max(v[q] & 0x7fffu, (v[q] >> 16) & 0x7fffu));
+  const int E = (int)(m >> 7) + ((m & 0x78u) == 0x78u ? 1 : 0);  // biased binade of the rounded maximum
+  const int e = min(127, max(-126, E - 127 - 2));
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e (e <= 126 for bf16 inputs)
+  uint64_t out[3] = {0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t h = (i & 1) ? (v[i >> 1] >> 16) : (v[i >> 1] & 0xffffu);
+    const float x = bf2f((uint16_t)(h & 0x7fffu)) * inv;
+    uint32_t c = x < 2.0f ? (uint32_t)__builtin_rintf(x * 8.0f)
+               : x < 4.0f ? (uint32_t)__builtin_rintf(x * 4.0f) + 8u
+                          : (uint32_t)__builtin_rintf(x * 2.0f) + 16u;
+    c = min(c, 31u);
+    if ((h & 0x8000u) && c) c |= 32u;
+    const int bit = 6 * i;
+    out[bit >> 6] |= (uint64_t)c << (bit & 63);
+    if ((bit & 63) > 58) out[(bit >> 6) + 1] |= (uint64_t)c >> (64 - (bit & 63));
+  }
+  uint64_t* dst = reinterpret_cast<uint64_t*>(codes + b * 24);
+  dst[0] = out[0];
+  dst[1] = out[1];
+  dst[2] = out[2];
+  scales[b] = (uint8_t)(e + 127);
+}
+
 // rows of bf16 -> MXFP4 codes [rows, cols/2] (low nibble = even element) and e8m0 scales
 // [rows, cols/32], with the quantiser of the decode kernel; one workgroup per row
 __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __restrict__ x, uint32_t* __restrict__ codes,
@@ -1190,7 +1359,8 @@ struct gdn_block {
   int kr;             // K range of a projection workgroup
   bool fold;          // out_proj folded in
   int o, ko;          // out_proj workgroups (4 tiles of 16 columns of H each) and K (nv * dv)
-  bool mx;
+  int fmt;            // kFmtBf16, kFmtMx4 or kFmtMx6 (the in_proj_qkvz format)
+  bool mx;            // MXFP4: the activations are quantised too (a second scratch image)
   void* scratch;
   uint16_t* xn;
   uint32_t* xq;
@@ -1209,7 +1379,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // K range of a projection workgroup: the largest divisor of H up to kKr in whole units
-// (4 waves x 32-wide bf16 steps, or 512-wide MXFP4 units); 0 if there is none
+// (4 waves x 32-wide bf16 steps, or 512 K for MXFP4 and MXFP6, whose scale dwords cover
+// 512 K); 0 if there is none
 int k_range(int H, bool mx) {
   const int unit = mx ? 512 : 128;
   for (int kr = kKr; kr >= unit; kr -= unit)
@@ -1230,15 +1401,17 @@ std::string check_config(const gdn_block_config* c) {
   if (c->conv_width != kConvW) add("conv_width must be 4");
   if (c->num_state_slots < 2) add("num_state_slots must be at least 2 (slot 0 is the pad slot)");
   if (c->max_rows < 1 || c->max_rows > GDN_MAX_ROWS) add("max_rows must be in 1..16");
-  if (c->qkvz_format != GDN_FMT_BF16 && c->qkvz_format != GDN_FMT_MXFP4)
-    add("qkvz_format must be GDN_FMT_BF16 or GDN_FMT_MXFP4");
-  if (c->qkvz_format == GDN_FMT_MXFP4 && c->hidden % 512 != 0)
-    add("MXFP4 in_proj_qkvz needs hidden to be a multiple of 512 (got " + std::to_string(c->hidden) + ")");
+  const bool scaled = c->qkvz_format == GDN_FMT_MXFP4 || c->qkvz_format == GDN_FMT_MXFP6;
+  if (c->qkvz_format != GDN_FMT_BF16 && !scaled)
+    add("qkvz_format must be GDN_FMT_BF16, GDN_FMT_MXFP4 or GDN_FMT_MXFP6");
+  if (scaled && c->hidden % 512 != 0)
+    add(std::string(c->qkvz_format == GDN_FMT_MXFP4 ? "MXFP4" : "MXFP6") +
+        " in_proj_qkvz needs hidden to be a multiple of 512 (got " + std::to_string(c->hidden) + ")");
   if (c->hidden > 0 && c->hidden % 256 == 0) {
-    const int kr = k_range(c->hidden, c->qkvz_format == GDN_FMT_MXFP4);
+    const int kr = k_range(c->hidden, scaled);
     if (kr == 0 || c->hidden / kr > kMaxSplits)
       add("hidden must split into at most " + std::to_string(kMaxSplits) + " K ranges of a multiple of " +
-          (c->qkvz_format == GDN_FMT_MXFP4 ? "512" : "128") + " up to 1024 (got " + std::to_string(c->hidden) + ")");
+          (scaled ? "512" : "128") + " up to 1024 (got " + std::to_string(c->hidden) + ")");
   }
   if (c->ssm_state_dtype != GDN_STATE_F32 && c->ssm_state_dtype != GDN_STATE_BF16)
     add("ssm_state_dtype must be GDN_STATE_F32 or GDN_STATE_BF16");
@@ -1264,37 +1437,39 @@ int fail(gdn_block* b, int code, const std::string& msg) {
   return code;
 }
 
-template <bool PACKED, bool MX, int DK, typename ST>
+template <bool PACKED, int FMT, int DK, typename ST>
 void launch_st(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
   if (b->fold)
-    hipLaunchKernelGGL((decode_kernel<PACKED, MX, DK, ST, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, true>), dim3(grid), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_kernel<PACKED, MX, DK, ST, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, false>), dim3(grid), dim3(kThreads), 0, st, a);
 }
 
-template <bool PACKED, bool MX, int DK>
+template <bool PACKED, int FMT, int DK>
 void launch_dk(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
   if (b->cfg.ssm_state_dtype == GDN_STATE_F32)
-    launch_st<PACKED, MX, DK, float>(b, a, grid, st);
+    launch_st<PACKED, FMT, DK, float>(b, a, grid, st);
   else
-    launch_st<PACKED, MX, DK, uint16_t>(b, a, grid, st);
+    launch_st<PACKED, FMT, DK, uint16_t>(b, a, grid, st);
 }
 
-template <bool PACKED, bool MX>
+template <bool PACKED, int FMT>
 void launch_fmt(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
   switch (b->cfg.head_k_dim) {
-    case 32: launch_dk<PACKED, MX, 32>(b, a, grid, st); break;
-    case 64: launch_dk<PACKED, MX, 64>(b, a, grid, st); break;
-    default: launch_dk<PACKED, MX, 128>(b, a, grid, st); break;
+    case 32: launch_dk<PACKED, FMT, 32>(b, a, grid, st); break;
+    case 64: launch_dk<PACKED, FMT, 64>(b, a, grid, st); break;
+    default: launch_dk<PACKED, FMT, 128>(b, a, grid, st); break;
   }
 }
 
 template <bool PACKED>
 void launch(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
-  if (b->mx)
-    launch_fmt<PACKED, true>(b, a, grid, st);
+  if (b->fmt == kFmtMx4)
+    launch_fmt<PACKED, kFmtMx4>(b, a, grid, st);
+  else if (b->fmt == kFmtMx6)
+    launch_fmt<PACKED, kFmtMx6>(b, a, grid, st);
   else
-    launch_fmt<PACKED, false>(b, a, grid, st);
+    launch_fmt<PACKED, kFmtBf16>(b, a, grid, st);
 }
 
 }  // namespace
@@ -1321,15 +1496,16 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   b->tb = (b->nb + 15) / 16;
   b->t = b->tq + b->tb;
   b->steps = H / 32;
-  b->mx = cfg->qkvz_format == GDN_FMT_MXFP4;
+  b->fmt = cfg->qkvz_format == GDN_FMT_MXFP4 ? kFmtMx4 : cfg->qkvz_format == GDN_FMT_MXFP6 ? kFmtMx6 : kFmtBf16;
+  b->mx = b->fmt == kFmtMx4;
   b->fold = cfg->fold_out_proj == 1;
   b->o = H / 64;
   b->ko = nv * dv;
   // K ranges: a projection workgroup stages the activations of its range in LDS, so the
   // range is the largest divisor of H up to kKr in whole units (32-wide bf16 steps grouped
-  // by 4 waves, or 512-wide MXFP4 units). The split count depends on the shape only,
+  // by 4 waves, or 512 K with MXFP4 or MXFP6). The split count depends on the shape only,
   // never on the row count.
-  const int kr = k_range(H, b->mx);
+  const int kr = k_range(H, b->fmt != kFmtBf16);
   b->kr = kr;
   const int S = H / kr;
   b->splits = S;
@@ -1370,12 +1546,16 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
 }
 
 namespace {
-// tiled copy: [in_proj_qkvz tiles | (MXFP4) their scale blocks | in_proj_ba tiles]
+// tiled copy: [in_proj_qkvz tiles | (MXFP4, MXFP6) their scale blocks | in_proj_ba tiles |
+// (fold) out_proj tiles]
 size_t packed_qkvz_bytes(const gdn_block* b) {
   const size_t H = b->cfg.hidden;
-  return b->mx ? (size_t)b->nq * H / 2 : (size_t)b->tq * 16 * H * 2;
+  return b->fmt == kFmtMx4 ? (size_t)b->nq * H / 2
+       : b->fmt == kFmtMx6 ? (size_t)b->nq * H * 3 / 4 : (size_t)b->tq * 16 * H * 2;
 }
-size_t packed_scale_bytes(const gdn_block* b) { return b->mx ? (size_t)b->nq * b->cfg.hidden / 32 : 0; }
+size_t packed_scale_bytes(const gdn_block* b) {
+  return b->fmt != kFmtBf16 ? (size_t)b->nq * b->cfg.hidden / 32 : 0;
+}
 size_t packed_ba_bytes(const gdn_block* b) { return (size_t)b->tb * 16 * b->cfg.hidden * 2; }
 size_t packed_out_bytes(const gdn_block* b) { return b->fold ? (size_t)b->cfg.hidden * b->ko * 2 : 0; }
 }  // namespace
@@ -1389,23 +1569,26 @@ extern "C" int gdn_block_pack_weights(gdn_block_t b, const gdn_block_weights* w,
   if (!b) return GDN_E_INVALID_ARG;
   if (!w || !w->w_qkvz || !w->w_ba || !packed)
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w, w->w_qkvz, w->w_ba and packed must not be NULL");
-  if (b->mx && !w->w_qkvz_scales)
-    return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w->w_qkvz_scales must not be NULL for MXFP4");
+  if (b->fmt != kFmtBf16 && !w->w_qkvz_scales)
+    return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w->w_qkvz_scales must not be NULL for MXFP4 and MXFP6");
   if (b->fold && (!w->w_out || !aligned16(w->w_out)))
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: w->w_out must be a 16-byte aligned pointer (fold_out_proj)");
   if (!aligned16(w->w_qkvz) || !aligned16(w->w_ba) || !aligned16(packed) ||
-      (b->mx && !aligned16(w->w_qkvz_scales)))
+      (b->fmt != kFmtBf16 && !aligned16(w->w_qkvz_scales)))
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_pack_weights: pointers must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int H = b->cfg.hidden;
   uint8_t* out = static_cast<uint8_t*>(packed);
   uint16_t* out_ba = reinterpret_cast<uint16_t*>(out + packed_qkvz_bytes(b) + packed_scale_bytes(b));
-  if (!b->mx) {
+  if (b->fmt == kFmtBf16) {
     hipLaunchKernelGGL(pack_kernel, dim3(b->steps, b->t), dim3(64), 0, st, static_cast<const uint16_t*>(w->w_qkvz),
                        static_cast<const uint16_t*>(w->w_ba), reinterpret_cast<uint16_t*>(out), H, b->tq, b->nq, b->nb);
   } else {
     const uint8_t* codes = static_cast<const uint8_t*>(w->w_qkvz);
-    hipLaunchKernelGGL(pack_mx_codes_kernel, dim3(H / 128, b->tq), dim3(64), 0, st, codes, out, H);
+    if (b->fmt == kFmtMx4)
+      hipLaunchKernelGGL(pack_mx_codes_kernel, dim3(H / 128, b->tq), dim3(64), 0, st, codes, out, H);
+    else
+      hipLaunchKernelGGL(pack_mx6_codes_kernel, dim3(H / 128, b->tq), dim3(64), 0, st, codes, out, H);
     hipLaunchKernelGGL(pack_mx_scales_kernel, dim3(H / 512, b->tq), dim3(64), 0, st,
                        static_cast<const uint8_t*>(w->w_qkvz_scales),
                        reinterpret_cast<uint32_t*>(out + packed_qkvz_bytes(b)), H);
@@ -1440,7 +1623,8 @@ int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_wei
   }
   const bool packed = w->w_proj_packed != nullptr;
   const bool normed = c.input_normed == 1;
-  const void* scales = (b->mx && !packed) ? w->w_qkvz_scales : x;  // checked only when read
+  const bool scaled = b->fmt != kFmtBf16;
+  const void* scales = (scaled && !packed) ? w->w_qkvz_scales : x;  // checked only when read
   const void* res_p = normed ? x : residual;                     // not read with a normed input
   const void* nw_p = normed ? x : w->norm_w;
   const void* ptrs[] = {x, res_p, conv_state, ssm_state, state_idx, core_out, nw_p,
@@ -1449,7 +1633,7 @@ int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_wei
   const char* names[] = {"x", normed ? "x" : "residual", "conv_state", "ssm_state", "state_idx", "core_out",
                          normed ? "x" : "norm_w",
                          packed ? "w_proj_packed" : "w_qkvz", packed ? "w_proj_packed" : "w_ba", "conv_w",
-                         "A_log", "dt_bias", "gated_norm_w", (b->mx && !packed) ? "w_qkvz_scales" : "x"};
+                         "A_log", "dt_bias", "gated_norm_w", (scaled && !packed) ? "w_qkvz_scales" : "x"};
   for (size_t i = 0; i < sizeof(ptrs) / sizeof(ptrs[0]); ++i) {
     if (!ptrs[i]) return fail(b, GDN_E_INVALID_ARG, std::string("gdn_block_decode: ") + names[i] + " is NULL");
     if (!aligned16(ptrs[i]))
@@ -1464,14 +1648,14 @@ int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_wei
   a.wq = static_cast<const uint16_t*>(w->w_qkvz);
   a.wb = static_cast<const uint16_t*>(w->w_ba);
   a.wpk = static_cast<const uint16_t*>(w->w_proj_packed);
-  a.wpk_sc = packed && b->mx ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(w->w_proj_packed) +
+  a.wpk_sc = packed && scaled ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(w->w_proj_packed) +
                                                                  packed_qkvz_bytes(b))
                              : nullptr;
   a.wpk_ba = packed ? reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(w->w_proj_packed) +
                                                         packed_qkvz_bytes(b) + packed_scale_bytes(b))
                     : nullptr;
-  a.wqc = b->mx ? static_cast<const uint8_t*>(w->w_qkvz) : nullptr;
-  a.wqs = b->mx ? static_cast<const uint8_t*>(w->w_qkvz_scales) : nullptr;
+  a.wqc = scaled ? static_cast<const uint8_t*>(w->w_qkvz) : nullptr;
+  a.wqs = scaled ? static_cast<const uint8_t*>(w->w_qkvz_scales) : nullptr;
   a.conv_w = static_cast<const uint16_t*>(w->conv_w);
   a.conv_state = static_cast<uint16_t*>(conv_state);
   a.ssm = ssm_state;
@@ -1595,6 +1779,34 @@ extern "C" int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, voi
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     g_create_error = std::string("gdn_mxfp4_quantize: launch failed: ") + hipGetErrorString(e);
+    return GDN_E_HIP;
+  }
+  return GDN_OK;
+}
+
+extern "C" int gdn_mxfp6_round_weights(const void* w, int32_t rows, int32_t cols, void* codes, void* scales,
+                                       void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0) {
+    g_create_error = "gdn_mxfp6_round_weights: rows must be >= 0 and cols a positive multiple of 32 (got rows " +
+                     std::to_string(rows) + ", cols " + std::to_string(cols) + ")";
+    return GDN_E_INVALID_ARG;
+  }
+  if (!w || !codes || !scales) {
+    g_create_error = "gdn_mxfp6_round_weights: w, codes and scales must not be NULL";
+    return GDN_E_INVALID_ARG;
+  }
+  if (!aligned16(w) || (reinterpret_cast<uintptr_t>(codes) & 7u)) {
+    g_create_error = "gdn_mxfp6_round_weights: w must be 16-byte and codes 8-byte aligned";
+    return GDN_E_INVALID_ARG;
+  }
+  if (rows == 0) return GDN_OK;
+  const long long nblk = (long long)rows * (cols / 32);
+  hipLaunchKernelGGL(mx6_round_kernel, dim3((unsigned)((nblk + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(w), static_cast<uint8_t*>(codes),
+                     static_cast<uint8_t*>(scales), nblk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_create_error = std::string("gdn_mxfp6_round_weights: launch failed: ") + hipGetErrorString(e);
     return GDN_E_HIP;
   }
   return GDN_OK;

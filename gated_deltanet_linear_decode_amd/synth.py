@@ -14,7 +14,10 @@ round-to-nearest-even cast.
 
 MXFP4 weights are drawn directly as codes and scales (no quantiser runs
 here): a random sign and e2m1 magnitude per element and a random e8m0 block
-exponent near the one an N(0, 0.02) block of 32 would get.
+exponent near the one an N(0, 0.02) block of 32 would get. MXFP6 weights
+likewise: a random sign and E2M3 magnitude code per element (32 magnitudes,
+smaller ones more likely), packed 32 codes to 24 bytes (code i at bits
+6i..6i+5 of the block, little-endian), and a random e8m0 block exponent.
 """
 from __future__ import annotations
 
@@ -23,7 +26,7 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from .configs import FMT_MXFP4, SSM_BF16, GdnShape
+from .configs import FMT_MXFP4, FMT_MXFP6, SSM_BF16, GdnShape
 
 
 def _bf16(a: np.ndarray) -> torch.Tensor:
@@ -57,6 +60,16 @@ class GdnCall:
 
 # e2m1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 drawn with these probabilities
 _E2M1_P = np.array([0.10, 0.18, 0.18, 0.15, 0.13, 0.12, 0.08, 0.06])
+# E2M3 magnitude codes 0..31 (0..0.875, 1..1.875, 2..3.75, 4..7.5): weights per code
+_E2M3_W = np.array([4.0] * 8 + [3.0] * 8 + [4.0] * 8 + [2.0] * 8)
+_E2M3_P = _E2M3_W / _E2M3_W.sum()
+
+
+def pack_6bit_blocks(codes: np.ndarray) -> np.ndarray:
+    """[N, K] 6-bit codes -> [N, K/32, 24] bytes, code i of a block at bits 6i..6i+5."""
+    n, k = codes.shape
+    bits = ((codes.reshape(n, k // 32, 32, 1) >> np.arange(6, dtype=np.uint8)) & 1).astype(np.uint8)
+    return np.packbits(bits.reshape(n, k // 32, 192), axis=-1, bitorder="little")
 
 
 def make_weights(shape: GdnShape, seed: int, *, gated_norm_stress: bool = False) -> GdnWeights:
@@ -73,6 +86,12 @@ def make_weights(shape: GdnShape, seed: int, *, gated_norm_stress: bool = False)
         scales = (127 - 7 + rng.integers(-1, 1, size=(s.n_qkvz, H // 32))).astype(np.uint8)
         w_qkvz = torch.from_numpy(packed)
         w_scales = torch.from_numpy(scales)
+    elif s.qkvz_format == FMT_MXFP6:
+        mag = rng.choice(32, size=(s.n_qkvz, H), p=_E2M3_P).astype(np.uint8)
+        sign = rng.integers(0, 2, size=(s.n_qkvz, H), dtype=np.uint8) << 5
+        w_qkvz = torch.from_numpy(pack_6bit_blocks(mag | sign))
+        # an N(0, 0.02) block's maximum is about 0.045 = 5.8 * 2^-7: scale 2^-7 or 2^-6
+        w_scales = torch.from_numpy((127 - 7 + rng.integers(0, 2, size=(s.n_qkvz, H // 32))).astype(np.uint8))
     else:
         w_qkvz = _bf16(rng.normal(0.0, 0.02, (s.n_qkvz, H)).astype(np.float32))
         w_scales = None

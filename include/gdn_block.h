@@ -9,7 +9,9 @@
  *      xn = bf16(h * (mean(h^2) + eps)^-1/2 * (1 + norm_w));
  *   2. in_proj_qkvz and in_proj_ba: y = bf16(W xn), bf16 weights, or MXFP4
  *      in_proj_qkvz with xn quantised to MXFP4 per 32-element block
- *      ("vLLM PR #60833", Details / MoE and MXFP4 layouts);
+ *      ("vLLM PR #60833", Details / MoE and MXFP4 layouts), or MXFP6 E2M3
+ *      in_proj_qkvz with bf16 xn (W6A16: "vLLM PR #60833", a reviewer's comment
+ *      proposing MXFP6 for the GDN projections);
  *   3. causal depthwise conv update (width 4, no bias) + SiLU over the q|k|v
  *      channels, conv state rolled in place;
  *   4. g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b); q, k
@@ -30,8 +32,12 @@
  *   norm_w            [H] bf16 (Gemma form: the scale is 1 + norm_w)
  *   w_qkvz (BF16)     [Nqkvz, H] bf16, Nqkvz = 2*nk*dk + 2*nv*dv, K contiguous
  *   w_qkvz (MXFP4)    [Nqkvz, H/2] uint8 e2m1 codes, low nibble = even k,
- *   w_qkvz_scales     [Nqkvz, H/32] uint8 e8m0 (2^(byte-127)), MXFP4 only
- *                     (MXFP4 needs H to be a multiple of 512)
+ *   w_qkvz (MXFP6)    [Nqkvz, H/32, 24] uint8: each block of 32 E2M3 codes (sign at
+ *                     bit 5, 2 exponent bits with bias 1, 3 mantissa bits) packed into
+ *                     24 bytes, code i at bits 6i..6i+5 of the block read as one
+ *                     little-endian number
+ *   w_qkvz_scales     [Nqkvz, H/32] uint8 e8m0 (2^(byte-127)), MXFP4 and MXFP6 only
+ *                     (MXFP4 and MXFP6 need H to be a multiple of 512)
  *                     Output columns are grouped per key head g:
  *                     [q_g (dk) | k_g (dk) | v_g (r*dv) | z_g (r*dv)], r = nv/nk.
  *   w_ba              [2*nv, H] bf16, grouped per key head: [b_g (r) | a_g (r)]
@@ -50,7 +56,9 @@
  * consecutive 1 KiB blocks in the operand order of the matrix cores, so every load
  * instruction of the projection reads 1 KiB of contiguous memory: bf16 tiles in
  * 32-wide steps; MXFP4 code tiles in 128-wide steps, followed by their scales, one
- * dword per lane per 4 steps. Pass it as w_proj_packed; w_qkvz, w_qkvz_scales and w_ba
+ * dword per lane per 4 steps; MXFP6 tiles in 128-wide steps of 1.5 KiB (each lane's
+ * 24 code bytes split as 16 + 8, the 16-byte parts of the 64 lanes first), followed by
+ * their scales like MXFP4's. Pass it as w_proj_packed; w_qkvz, w_qkvz_scales and w_ba
  * are then not read. The copy is made once (like the pages' shuffled weight copies
  * made before graph capture, "SGLang PR #43558", Modifications / Weights) and has the
  * size of the matrices it copies.
@@ -82,6 +90,8 @@ extern "C" {
 
 #define GDN_FMT_BF16 0   /* in_proj_qkvz stored as bf16 */
 #define GDN_FMT_MXFP4 1  /* in_proj_qkvz stored as OCP MXFP4: e2m1 codes + e8m0 per 32 K */
+#define GDN_FMT_MXFP6 2  /* in_proj_qkvz stored as OCP MXFP6 E2M3 codes + e8m0 per 32 K;
+                            the activations stay bf16 */
 
 #define GDN_STATE_F32 0
 #define GDN_STATE_BF16 1
@@ -89,7 +99,7 @@ extern "C" {
 #define GDN_MAX_ROWS 16
 
 typedef struct gdn_block_config {
-  int32_t hidden;          /* H; a multiple of 256 (of 512 with MXFP4), at most 16384 */
+  int32_t hidden;          /* H; a multiple of 256 (of 512 with MXFP4 or MXFP6), at most 16384 */
   int32_t num_k_heads;     /* nk */
   int32_t head_k_dim;      /* dk: 32, 64 or 128 */
   int32_t num_v_heads;     /* nv; a multiple of nk */
@@ -97,7 +107,7 @@ typedef struct gdn_block_config {
   int32_t conv_width;      /* W; must be 4 */
   int32_t num_state_slots; /* slots in the conv and SSM state pools */
   int32_t max_rows;        /* largest row count a decode call may pass, 1..16 */
-  int32_t qkvz_format;     /* GDN_FMT_BF16 or GDN_FMT_MXFP4 */
+  int32_t qkvz_format;     /* GDN_FMT_BF16, GDN_FMT_MXFP4 or GDN_FMT_MXFP6 */
   int32_t ssm_state_dtype; /* GDN_STATE_F32 or GDN_STATE_BF16 */
   int32_t has_residual;    /* 0: the layer with no residual input (residual is written = x) */
   float norm_eps;          /* Gemma RMSNorm eps (1e-6) */
@@ -117,8 +127,9 @@ typedef struct gdn_block_config {
 
 typedef struct gdn_block_weights {
   const void* norm_w;        /* [H] bf16 */
-  const void* w_qkvz;        /* [Nqkvz, H] bf16 or [Nqkvz, H/2] e2m1 bytes */
-  const void* w_qkvz_scales; /* [Nqkvz, H/32] e8m0 bytes (MXFP4 only, else ignored) */
+  const void* w_qkvz;        /* [Nqkvz, H] bf16, [Nqkvz, H/2] e2m1 bytes or [Nqkvz, H/32, 24]
+                                E2M3 bytes */
+  const void* w_qkvz_scales; /* [Nqkvz, H/32] e8m0 bytes (MXFP4 and MXFP6, else ignored) */
   const void* w_ba;          /* [2*nv, H] bf16 */
   const void* conv_w;        /* [Cd, W] bf16 */
   const float* A_log;        /* [nv] f32 */
@@ -163,13 +174,13 @@ int gdn_block_decode_with_out_proj(gdn_block_t blk, const void* x, void* residua
                                    void* core_out, void* out, void* stream);
 
 /* Size in bytes of the tiled projection copy (16-row tiles of [in_proj_qkvz;
- * in_proj_ba], the last b|a tile zero-padded): Nqkvz*H*2 (bf16) or Nqkvz*H/2 +
- * Nqkvz*H/32 (MXFP4), plus ceil(2*nv/16) * 16 * H * 2, plus H * nv*dv * 2 with
+ * in_proj_ba], the last b|a tile zero-padded): Nqkvz*H*2 (bf16), Nqkvz*H/2 +
+ * Nqkvz*H/32 (MXFP4) or Nqkvz*H*3/4 + Nqkvz*H/32 (MXFP6), plus ceil(2*nv/16) * 16 * H * 2, plus H * nv*dv * 2 with
  * fold_out_proj (W_out in the same tiles). 0 for a NULL handle. */
 size_t gdn_block_packed_weight_bytes(gdn_block_t blk);
 
 /* Enqueue on `stream` the write of the tiled copy of w->w_qkvz (with w->w_qkvz_scales
- * for MXFP4), w->w_ba and, with fold_out_proj, w->w_out, all row-major as above, into
+ * for MXFP4 and MXFP6), w->w_ba and, with fold_out_proj, w->w_out, all row-major as above, into
  * `packed` (device memory of gdn_block_packed_weight_bytes bytes, 16-byte aligned,
  * caller-owned). */
 int gdn_block_pack_weights(gdn_block_t blk, const gdn_block_weights* w, void* packed, void* stream);
@@ -181,6 +192,19 @@ int gdn_block_pack_weights(gdn_block_t blk, const gdn_block_weights* w, void* pa
  * rows == 0 enqueues nothing. Asynchronous on `stream`; allocates nothing. Errors are
  * reported like a failed gdn_block_create (gdn_block_last_error(NULL)). */
 int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, void* codes, void* scales, void* stream);
+
+/* Round `rows` rows of `cols` bf16 weights (w, [rows, cols], device, 16-byte aligned)
+ * to MXFP6 E2M3, one block of 32 along a row at a time, and write them in the layout
+ * w_qkvz takes: codes [rows, cols/32, 24] uint8 (device, 8-byte aligned) and scales
+ * [rows, cols/32] uint8 e8m0 (device). The rule is the one the pages give for making
+ * the weights ("vLLM PR #60833", a reviewer's comment proposing MXFP6, step 2): the
+ * block maximum is rounded to 3 mantissa bits (a carry moving into the exponent), the
+ * scale is 2^(E - 2) with E the exponent of that rounded maximum, clamped to
+ * 2^[-126, 127] (an all-zero block keeps 2^-126); each value is rounded to the nearest
+ * E2M3 value, ties to the even code, at most 7.5; a zero code carries no sign. cols must
+ * be a positive multiple of 32; rows == 0 enqueues nothing. Asynchronous on `stream`;
+ * allocates nothing. Errors are reported like gdn_mxfp4_quantize's. */
+int gdn_mxfp6_round_weights(const void* w, int32_t rows, int32_t cols, void* codes, void* scales, void* stream);
 
 /* Read and clear the handle's sticky error word (synchronous; not for the hot
  * path). Inside a decode, every wait for another workgroup is bounded; a wait
@@ -194,7 +218,7 @@ int gdn_block_check(gdn_block_t blk, uint32_t* error_word);
 void gdn_block_destroy(gdn_block_t blk);
 
 /* The last error message of a handle, or of this thread's last failed
- * gdn_block_create or gdn_mxfp4_quantize when blk is NULL. Never NULL; "" when there
+ * gdn_block_create, gdn_mxfp4_quantize or gdn_mxfp6_round_weights when blk is NULL. Never NULL; "" when there
  * was none. */
 const char* gdn_block_last_error(gdn_block_t blk);
 

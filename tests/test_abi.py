@@ -95,6 +95,28 @@ def test_mxfp4_needs_hidden_multiple_of_512():
     assert e.value.code == abi.GDN_E_UNSUPPORTED and "512" in str(e.value)
 
 
+def test_mxfp6_needs_hidden_multiple_of_512():
+    with pytest.raises(abi.GdnError) as e:
+        abi.gdn_block_create(_cfg(qkvz_format=abi.GDN_FMT_MXFP6))  # the tiny shape has H = 256
+    assert e.value.code == abi.GDN_E_UNSUPPORTED and "MXFP6" in str(e.value) and "512" in str(e.value)
+
+
+def test_mxfp6_rounding_arguments_are_checked_on_the_host():
+    lib = abi.load()
+    fake = 1 << 20  # an aligned address that is never dereferenced: every call below is refused
+    for rows, cols, w, codes, scales, needle in [
+        (1, 48, fake, fake, fake, "multiple of 32"),
+        (-1, 32, fake, fake, fake, "rows"),
+        (1, 0, fake, fake, fake, "cols"),
+        (1, 32, fake, None, fake, "NULL"),
+        (1, 32, fake + 8, fake, fake, "aligned"),
+        (1, 32, fake, fake + 4, fake, "aligned"),
+    ]:
+        assert lib.gdn_mxfp6_round_weights(w, rows, cols, codes, scales, None) == abi.GDN_E_INVALID_ARG
+        assert needle in abi.gdn_block_last_error(None)
+    assert lib.gdn_mxfp6_round_weights(fake, 0, 32, fake, fake, None) == abi.GDN_OK  # nothing to do
+
+
 def test_quantize_arguments_are_checked_on_the_host():
     lib = abi.load()
     fake = 1 << 20  # an aligned address that is never dereferenced: every call below is refused

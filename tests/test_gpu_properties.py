@@ -22,7 +22,8 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tp8_rank_f32_state_pads", "tp8_rank_mxfp4",
-                                  "tp8_rank_mxfp4_normed_input", "tp8_rank_bf16_state_out_proj"])
+                                  "tp8_rank_mxfp4_normed_input", "tp8_rank_bf16_state_out_proj",
+                                  "tp8_rank_mxfp6"])
 def test_batch_invariance(name):
     """A probe row's outputs do not change with the other rows or the width."""
     shape = configs.ALL[name].with_(num_state_slots=40, rows=(16,), pad_rows=False)
