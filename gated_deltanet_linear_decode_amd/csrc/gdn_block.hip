@@ -17,7 +17,9 @@
 //                     one e8m0 scale per 32) into a second scratch image.
 //   [R*P, R*P+G)      projection: in_proj_qkvz and in_proj_ba as one skinny GEMM on the
 //                     matrix cores: bf16 weights on v_mfma_f32_16x16x32_bf16, MXFP4 weights
-//                     on v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 x fp4 with per-32 scales);
+//                     on v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 x fp4 with per-32 scales),
+//                     MXFP6 E2M3 weights converted to bf16 in registers (exactly) and then
+//                     on the bf16 instruction with the bf16 activations;
 //                     16 weight rows x 16 decode rows per instruction. Each workgroup owns
 //                     one 16-channel tile and one split of K. It issues its weight loads
 //                     first, then waits for the norm rows, multiplies, and publishes its f32
