@@ -27,4 +27,5 @@ from .gdn import (  # noqa: F401
     gated_delta_recurrence,
     gated_rmsnorm,
     decode_block,
+    verify_block,
 )

@@ -201,3 +201,148 @@ def test_normed_input_equals_the_block_from_its_norm_output():
     assert normed["residual"] is None
     for k in ("core", "conv_state", "ssm_state", "y_qkvz", "y_ba"):
         assert np.array_equal(normed[k], full[k]), k
+
+
+# ----------------------------------------------------------------------------------------
+# verify: several tokens per sequence, the state after each kept
+
+
+def _verify_inputs(shape, R, T, seed):
+    """R sequences of T tokens: sources 1..R (sequence 1 a pad), destinations from a
+    disjoint range, one snapshot not kept, and sequence 0 continuing in its own slot."""
+    call = synth.make_call(shape, R * T, seed)
+    src = np.arange(1, R + 1, dtype=np.int32)
+    src[1] = -1
+    dst = (R + 1 + np.arange(R * T, dtype=np.int32)).reshape(R, T)
+    dst[0, T - 1] = src[0]
+    dst[2, 0] = 0
+    return call, src, dst
+
+
+def _library_verify(shape, w, call, src, dst):
+    """Verify composed from torch float64 library routines: the front row by row as in
+    _library_block, then per sequence conv1d over [old window; the tokens] at once and the
+    delta rule carried across the tokens unrounded."""
+    import torch
+    import torch.nn.functional as F
+    rb = lambda t: torch.from_numpy(og.bf16_to_f64(og.f64_to_bf16(t.numpy())))  # noqa: E731
+    d = lambda t: t.double()                                                    # noqa: E731
+    nk, dk, nv, dv, r = shape.num_k_heads, shape.head_k_dim, shape.num_v_heads, shape.head_v_dim, \
+        shape.heads_per_group
+    R, T = dst.shape
+    h = rb(d(call.x) + d(call.residual)) if shape.has_residual else d(call.x)
+    xn = rb(F.rms_norm(h, (shape.hidden,), weight=1 + d(w.norm_w), eps=shape.norm_eps))
+    yq = rb(xn @ d(w.w_qkvz).T).reshape(-1, nk, shape.group_width)
+    yb = rb(xn @ d(w.w_ba).T).reshape(-1, nk, 2 * r)
+    q, k = yq[..., :dk], yq[..., dk:2 * dk]
+    v = yq[..., 2 * dk:2 * dk + r * dv].reshape(-1, nv, dv)
+    z = yq[..., 2 * dk + r * dv:].reshape(-1, nv, dv)
+    b, a = yb[..., :r].reshape(-1, nv), yb[..., r:].reshape(-1, nv)
+    qkv = torch.cat([q.reshape(-1, nk * dk), k.reshape(-1, nk * dk), v.reshape(-1, nv * dv)], -1)
+    S_pool = d(call.ssm_state).clone()
+    C_pool = d(call.conv_state).clone()
+    core = torch.zeros(R * T, nv * dv, dtype=torch.float64)
+    bf16_state = shape.ssm_state_dtype == "bf16"
+    for s_, slot in enumerate(src.tolist()):
+        if slot <= 0:
+            continue
+        rows = slice(s_ * T, (s_ + 1) * T)
+        seq = torch.cat([d(call.conv_state)[slot], qkv[rows]], 0)           # [W-1+T, Cd]
+        conv = F.conv1d(seq.T[None], d(w.conv_w)[:, None, :], groups=shape.conv_dim)[0].T   # [T, Cd]
+        c = rb(F.silu(conv))
+        S = d(call.ssm_state)[slot].clone()                                  # [nv, dk, dv]
+        for t in range(T):
+            row = s_ * T + t
+            cq_raw = c[t, :nk * dk].reshape(nk, dk)
+            ck_raw = c[t, nk * dk:2 * nk * dk].reshape(nk, dk)
+            cq = cq_raw / (cq_raw.square().sum(-1, keepdim=True) + shape.l2norm_eps).sqrt() / dk ** 0.5
+            ck = ck_raw / (ck_raw.square().sum(-1, keepdim=True) + shape.l2norm_eps).sqrt()
+            cv = c[t, 2 * nk * dk:].reshape(nv, dv)
+            g = -torch.exp(d(w.A_log)) * F.softplus(a[row] + d(w.dt_bias))
+            beta = torch.sigmoid(b[row])
+            for hv in range(nv):
+                kk, qq = ck[hv // r], cq[hv // r]
+                Sh = torch.exp(g[hv]) * S[hv]
+                S[hv] = Sh + torch.outer(kk, beta[hv] * (cv[hv] - Sh.T @ kk))
+                o = rb(S[hv].T @ qq)
+                core[row, hv * dv:(hv + 1) * dv] = rb(
+                    F.rms_norm(o, (dv,), weight=d(w.gated_norm_w), eps=shape.gated_norm_eps) * F.silu(z[row, hv]))
+            dslot = int(dst[s_, t])
+            if 0 < dslot < shape.num_state_slots:
+                C_pool[dslot] = seq[t + 1:t + shape.conv_width]
+                S_pool[dslot] = rb(S) if bf16_state else S.float().double()
+    return core, S_pool, C_pool
+
+
+@pytest.mark.parametrize("bf16_state", [False, True])
+def test_verify_against_library_composition(bf16_state):
+    shape = configs.TINY.with_(num_state_slots=24, ssm_state_dtype="bf16" if bf16_state else "f32")
+    R, T = 4, 3
+    w = synth.make_weights(shape, 12)
+    call, src, dst = _verify_inputs(shape, R, T, 12)
+    out = og.verify_block(oracle_cfg(shape), oracle_weights(w), u16(call.x), u16(call.residual),
+                          u16(call.conv_state), oracle_state(call.ssm_state), src, dst)
+    core, S_pool, C_pool = _library_verify(shape, w, call, src, dst)
+    assert np.array_equal(og.bf16_to_f64(out["core"]), core.numpy())
+    assert np.array_equal(og.bf16_to_f64(out["conv_state"]), C_pool.numpy())
+    got_S = og.bf16_to_f64(out["ssm_state"]) if bf16_state else out["ssm_state"].astype(np.float64)
+    assert np.allclose(got_S, S_pool.numpy(), rtol=0, atol=1e-7 if not bf16_state else 0)
+
+
+def test_verify_one_token_is_a_decode_step():
+    """tokens = 1 with each sequence's destination its own source is decode_block, bit for bit."""
+    shape = configs.TINY.with_(num_state_slots=10, pad_rows=True)
+    w = synth.make_weights(shape, 13)
+    call = synth.make_call(shape, 5, 13)
+    src = call.state_idx.numpy().copy()
+    dec = run_oracle(shape, w, call)
+    ver = og.verify_block(oracle_cfg(shape), oracle_weights(w), u16(call.x), u16(call.residual),
+                          u16(call.conv_state), oracle_state(call.ssm_state), src, src[:, None])
+    for k in ("core", "residual", "conv_state", "ssm_state"):
+        assert np.array_equal(ver[k], dec[k]), k
+
+
+def test_verify_keeps_only_the_named_snapshots():
+    """Pad sequences and unkept snapshots write nothing; every slot not named as a valid
+    destination keeps its bits; a pad sequence's core rows are +0."""
+    shape = configs.TINY.with_(num_state_slots=24)
+    R, T = 4, 3
+    w = synth.make_weights(shape, 14)
+    call, src, dst = _verify_inputs(shape, R, T, 14)
+    out = og.verify_block(oracle_cfg(shape), oracle_weights(w), u16(call.x), u16(call.residual),
+                          u16(call.conv_state), oracle_state(call.ssm_state), src, dst)
+    written = set(int(s) for s in dst.reshape(-1) if 0 < s < shape.num_state_slots)
+    for slot in range(shape.num_state_slots):
+        if slot not in written:
+            assert np.array_equal(out["conv_state"][slot], u16(call.conv_state)[slot]), slot
+            assert np.array_equal(out["ssm_state"][slot], oracle_state(call.ssm_state)[slot]), slot
+    assert np.all(out["core"][1 * T:2 * T] == 0)
+    assert np.any(out["core"][0] != 0)
+
+
+def test_verify_chain_of_decodes_with_f32_state():
+    """With an f32 pool, T tokens in one verify step end where T decode steps end (the
+    state is carried unrounded inside the step, rounded to f32 between decode steps)."""
+    shape = configs.TINY.with_(num_state_slots=24)
+    R, T = 3, 4
+    w = synth.make_weights(shape, 15)
+    call, src, dst = _verify_inputs(shape, R, T, 15)
+    src[1] = 2  # no pad here
+    dst[2, 0] = R + 1 + 2 * T
+    ver = og.verify_block(oracle_cfg(shape), oracle_weights(w), u16(call.x), u16(call.residual),
+                          u16(call.conv_state), oracle_state(call.ssm_state), src, dst)
+    conv, ssm = u16(call.conv_state), oracle_state(call.ssm_state)
+    slots = src.copy()
+    for t in range(T):
+        rows = np.arange(R) * T + t
+        dec = og.decode_block(oracle_cfg(shape), oracle_weights(w), u16(call.x)[rows], u16(call.residual)[rows],
+                              conv, ssm, slots)
+        assert np.array_equal(dec["core"], ver["core"][rows]), t
+        conv, ssm = dec["conv_state"], dec["ssm_state"]
+        for s_ in range(R):   # move each sequence's state to its destination slot
+            conv[dst[s_, t]] = conv[slots[s_]]
+            ssm[dst[s_, t]] = ssm[slots[s_]]
+        slots = dst[:, t].copy()
+    for s_ in range(R):
+        assert np.array_equal(ver["conv_state"][dst[s_, T - 1]], conv[dst[s_, T - 1]])
+        assert np.allclose(ver["ssm_state"][dst[s_, T - 1]], ssm[dst[s_, T - 1]], rtol=0, atol=1e-6)
