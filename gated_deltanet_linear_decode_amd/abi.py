@@ -24,7 +24,8 @@ GDN_MAX_ROWS = 16
 
 EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error",
             "gdn_block_packed_weight_bytes", "gdn_block_pack_weights", "gdn_block_check",
-            "gdn_mxfp4_quantize", "gdn_block_decode_with_out_proj", "gdn_mxfp6_round_weights")
+            "gdn_mxfp4_quantize", "gdn_block_decode_with_out_proj", "gdn_mxfp6_round_weights",
+            "gdn_block_verify")
 
 
 class GdnBlockConfig(ctypes.Structure):
@@ -88,6 +89,9 @@ def load() -> ctypes.CDLL:
         lib.gdn_mxfp4_quantize.restype = c_int
         lib.gdn_mxfp6_round_weights.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
         lib.gdn_mxfp6_round_weights.restype = c_int
+        lib.gdn_block_verify.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(GdnBlockWeights), c_void_p, c_void_p,
+                                         c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]
+        lib.gdn_block_verify.restype = c_int
         _lib = lib
     return _lib
 
@@ -117,6 +121,14 @@ def gdn_block_decode_with_out_proj(handle, x: int, residual: int, weights: GdnBl
                                    stream: int) -> None:
     rc = load().gdn_block_decode_with_out_proj(handle, x, residual, ctypes.byref(weights), conv_state, ssm_state,
                                                state_idx, rows, core_out, out, stream)
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(handle))
+
+
+def gdn_block_verify(handle, x: int, residual: int, weights: GdnBlockWeights, conv_state: int, ssm_state: int,
+                     src_idx: int, dst_idx: int, rows: int, tokens: int, core_out: int, stream: int) -> None:
+    rc = load().gdn_block_verify(handle, x, residual, ctypes.byref(weights), conv_state, ssm_state, src_idx,
+                                 dst_idx, rows, tokens, core_out, stream)
     if rc != GDN_OK:
         raise GdnError(rc, gdn_block_last_error(handle))
 

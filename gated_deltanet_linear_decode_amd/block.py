@@ -134,3 +134,27 @@ class GdnBlock:
             abi.gdn_block_decode_with_out_proj(self.handle, px, pr, ws, pc, ps, pi, R, po, pout, stream)
         else:
             abi.gdn_block_decode(self.handle, px, pr, ws, pc, ps, pi, R, po, stream)
+
+    def verify(self, x, residual, weights, conv_state, ssm_state, src_idx, dst_idx, core_out,
+               stream=None, weights_struct=None):
+        """Enqueue one verify step: `rows` sequences of `tokens` tokens (dst_idx is
+        [rows, tokens] int32; x, residual and core_out have rows * tokens rows, token t
+        of sequence r at row r * tokens + t). See gdn_block_verify in the header."""
+        s, d = self.shape, self.device
+        rows, tokens = dst_idx.shape
+        R = rows * tokens
+        H = s.hidden
+        ws = weights_struct if weights_struct is not None else self.weights_struct(weights)
+        ssm_dtype = torch.bfloat16 if s.ssm_state_dtype == SSM_BF16 else torch.float32
+        px = _check(x, "x", torch.bfloat16, (R, H), d)
+        pr = None if s.input_normed else _check(residual, "residual", torch.bfloat16, (R, H), d)
+        pc = _check(conv_state, "conv_state", torch.bfloat16,
+                    (s.num_state_slots, s.conv_width - 1, s.conv_dim), d)
+        ps = _check(ssm_state, "ssm_state", ssm_dtype,
+                    (s.num_state_slots, s.num_v_heads, s.head_k_dim, s.head_v_dim), d)
+        pi = _check(src_idx, "src_idx", torch.int32, (rows,), d)
+        pd = _check(dst_idx, "dst_idx", torch.int32, (rows, tokens), d)
+        po = _check(core_out, "core_out", torch.bfloat16, (R, s.value_dim), d)
+        if stream is None:
+            stream = torch.cuda.current_stream(d).cuda_stream
+        abi.gdn_block_verify(self.handle, px, pr, ws, pc, ps, pi, pd, rows, tokens, po, stream)

@@ -229,7 +229,8 @@ struct Args {
   const uint16_t* conv_w;    // [Cd, 4]
   uint16_t* conv_state;      // [slots, 3, Cd]
   void* ssm;                 // [slots, nv, dk, dv] f32 or bf16
-  const int32_t* idx;        // [R]
+  const int32_t* idx;        // [Rs] each sequence's state slot (decode: one token per sequence)
+  const int32_t* dst;        // [Rs, Tk] slots that receive the state after each token (verify), or null
   const float* A_log;        // [nv]
   const uint16_t* dt_bias;   // [nv]
   const uint16_t* gnw;       // [dv]
@@ -244,7 +245,8 @@ struct Args {
   float* part;               // [S, R, Nq + Nb] split partials of the projections
   uint32_t* sync;            // sync word lines
   // sizes
-  int H, R, has_res, P;  // P: norm workgroups per row (0 with a normed input)
+  int H, R, has_res, P;  // R: token rows (Rs sequences x Tk tokens); P: norm workgroups per row
+  int Rs, Tk;            // sequences and tokens per sequence (decode: Tk = 1)
   int normed;            // x is already the norm's output xn
   int fold, O, Ko;       // out_proj folded in; its workgroups (4 16-column tiles of H each); K = nv*dv
   int T, Tq, Tb, Nq, Nb, steps;  // tiles (all, in_proj_qkvz, in_proj_ba), channels, 32-wide K steps of H
@@ -941,7 +943,23 @@ __device__ __forceinline__ float proj_one(const Args& a, int n, int ch) {
              : a.S <= 8 ? sum_splits1<8>(base, stride, a.S) : sum_splits1<16>(base, stride, a.S));
 }
 
-template <int DK, typename ST>
+// conv channel state after the token y: drop the oldest input, append y
+__device__ __forceinline__ void conv_roll(ConvIn& c, float y) {
+#pragma unroll
+  for (int j = 0; j < kConvW - 2; ++j) c.prev[j] = c.prev[j + 1];
+  c.prev[kConvW - 2] = f2bf(y);
+}
+
+// One workgroup per (sequence, value head). A decode step is a sequence of one token
+// whose state goes back to its own slot; a verify step runs the sequence's Tk tokens one
+// after the other from its source slot, keeping the state in registers, and stores the
+// state (and conv window) after token t into the slot dst[t] when that is a valid slot,
+// so a caller can continue from any accepted token (the follow-up the pages leave open:
+// "sgl-amd-mono PR #89", Modifications, and "vLLM PR #60833", Limitations: K1 keeps no
+// state per draft token, so a rejected draft could not roll back). MULTI instantiates the
+// token loop; without it the loop runs once and compiles to the single-token code (the
+// loop-carried state tile costs registers the decode launches should not pay for).
+template <int DK, typename ST, bool MULTI>
 __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   constexpr int DV = DK;
   // State tile layout: wave w owns the columns [w DV/4, (w+1) DV/4) as QW quads of 4
@@ -952,13 +970,15 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   constexpr int NRG = 64 / QW;         // row groups per wave
   constexpr int RPT = DK / NRG;        // state rows per lane
   static_assert(QW * NRG == 64 && RPT * NRG == DK && RPT >= 1 && DK <= 128, "tile shape");
-  const int n = rb / a.nv, h = rb - n * a.nv, tid = threadIdx.x;
+  const int seq = rb / a.nv, h = rb - seq * a.nv, tid = threadIdx.x;
+  const int Tk = MULTI ? a.Tk : 1;
   const int kap = h / a.r, hh = h - kap * a.r;
   const bool qk_owner = hh == a.r - 1;  // writes the key head's q|k conv state
-  const int slot = a.idx[n];
+  const int slot = a.idx[seq];
   const bool valid = slot > 0 && slot < a.slots;
   const int lane = tid & 63, rg = lane / QW, cq = (tid >> 6) * QW + lane % QW;
-  const size_t sbase = (((size_t)(valid ? slot : 0) * a.nv + h) * DK) * DV + 4 * cq;
+  const size_t tile = ((size_t)a.nv * DK) * DV;  // state elements per slot
+  const size_t hoff = ((size_t)h * DK) * DV + 4 * cq;
 
   // everything that does not depend on this launch's projections is loaded first
   float S[RPT][4];
@@ -966,7 +986,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   const bool qk_thread = tid < DK, v_thread = tid >= 128 && tid < 128 + DV;
   if (valid) {
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) StateIO<ST>::load(a.ssm, sbase + (size_t)(rg + NRG * m) * DV, S[m]);
+    for (int m = 0; m < RPT; ++m) StateIO<ST>::load(a.ssm, slot * tile + hoff + (size_t)(rg + NRG * m) * DV, S[m]);
     if (qk_thread) {
       conv_load(a, slot, kap * DK + tid, c0);
       conv_load(a, slot, a.nk * DK + kap * DK + tid, c1);
@@ -980,7 +1000,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
     // the old q|k conv rows are in registers: let the owner overwrite them
     wait_stores();
     __syncthreads();
-    if (tid == 0) add_agent(sy(a, sy_conv(a, n, kap)), 1u);
+    if (tid == 0) add_agent(sy(a, sy_conv(a, seq, kap)), 1u);
   }
 
   // every recurrence workgroup waits, pad rows included (see the counter clearing below)
@@ -988,125 +1008,132 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.S), sy(a, kSyError), kErrGroupWait);
   TRACE_POINT(1);
 
-  uint16_t* core = a.core + (size_t)n * a.nv * DV + (size_t)h * DV;
   uint32_t exit_ticket = 0;
   if (valid) {
     const int gbase = kap * a.GW;
-    // threads < DK: one quad of the head's channels each, q | k | v | z in DK / 4 quads apiece
-    if (tid < DK) {
-      const int blk = tid / (DK / 4), j = 4 * (tid % (DK / 4));
-      const int ch = gbase + (blk == 0 ? j : blk == 1 ? DK + j : blk == 2 ? 2 * DK + hh * DV + j
-                                                              : 2 * DK + a.r * DV + hh * DV + j);
-      *reinterpret_cast<f32x4_t*>(&sh.y[blk][j]) = proj_quad(a, n, ch);
-    }
-    // the two gates are independent chains: thread 128 takes b, thread 192 takes a
-    float yg = 0.0f;
-    if (tid == 128 || tid == 192) yg = proj_one(a, n, a.Nq + kap * 2 * a.r + (tid == 192 ? a.r : 0) + hh);
-    // past every wait of this workgroup: count it (loads complete in issue order, so the
-    // atomic goes after this wave's loads to keep its latency off their path)
-    if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
-    TRACE_POINT(5);
-    if (tid == 128) {
-      sh.scal[3] = __builtin_amdgcn_rcpf(1.0f + __expf(-yg));  // beta = sigmoid(b)
-    } else if (tid == 192) {
-      const float x = yg + dtb;
-      const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
-      sh.scal[2] = __expf(-__expf(alog) * sp);  // exp(g), g = -exp(A_log) softplus(a + dt_bias)
-    }
-    __syncthreads();
-    const int j = tid - 128;
-    float yq = 0.0f, yk = 0.0f;  // this thread's q and k projection outputs (bf16 values)
-    if (qk_thread) {
-      yq = sh.y[0][tid];
-      yk = sh.y[1][tid];
-      sh.qs[tid] = conv_out(c0, yq);
-      sh.ks[tid] = conv_out(c1, yk);
-    } else if (v_thread) {
-      const float yv = sh.y[2][j];
-      sh.vs[j] = conv_out(c0, yv);
-      conv_store(a, slot, c0, yv);
-    }
-    __syncthreads();
-    TRACE_POINT(2);
-    // One pass over the old state with the raw (not yet normalised) conv outputs k and q:
-    // per lane, the partial sums over its rows of S^T k and S^T q for its 4 columns and of
-    // k.k, q.q and k.q; then sums over the row groups by an xor butterfly inside the wave,
-    // after which every lane of a column quad holds the same totals.
-    float v[11] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (qk_owner && a.r > 1)  // the key head's other value heads have read the old q|k conv rows
+      wait_count(sy(a, sy_conv(a, seq, kap)), (uint32_t)(a.r - 1), sy(a, kSyError), kErrConvWait);
+#pragma unroll 1
+    for (int t = 0; t < Tk; ++t) {
+      const int n = seq * Tk + t;  // the token's projection row
+      const int dslot = MULTI ? a.dst[n] : slot;
+      const bool keep = dslot > 0 && dslot < a.slots;  // store the state after this token
+      if (t > 0) __syncthreads();  // the previous token is done with the shared arrays
+      // threads < DK: one quad of the head's channels each, q | k | v | z in DK / 4 quads apiece
+      if (tid < DK) {
+        const int blk = tid / (DK / 4), j = 4 * (tid % (DK / 4));
+        const int ch = gbase + (blk == 0 ? j : blk == 1 ? DK + j : blk == 2 ? 2 * DK + hh * DV + j
+                                                                : 2 * DK + a.r * DV + hh * DV + j);
+        *reinterpret_cast<f32x4_t*>(&sh.y[blk][j]) = proj_quad(a, n, ch);
+      }
+      // the two gates are independent chains: thread 128 takes b, thread 192 takes a
+      float yg = 0.0f;
+      if (tid == 128 || tid == 192) yg = proj_one(a, n, a.Nq + kap * 2 * a.r + (tid == 192 ? a.r : 0) + hh);
+      // past every wait of this workgroup: count it (loads complete in issue order, so the
+      // atomic goes after this wave's loads to keep its latency off their path)
+      if (t == 0 && tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
+      TRACE_POINT(5);
+      if (tid == 128) {
+        sh.scal[3] = __builtin_amdgcn_rcpf(1.0f + __expf(-yg));  // beta = sigmoid(b)
+      } else if (tid == 192) {
+        const float x = yg + dtb;
+        const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
+        sh.scal[2] = __expf(-__expf(alog) * sp);  // exp(g), g = -exp(A_log) softplus(a + dt_bias)
+      }
+      __syncthreads();
+      const int j = tid - 128;
+      if (qk_thread) {
+        const float yq = sh.y[0][tid], yk = sh.y[1][tid];
+        sh.qs[tid] = conv_out(c0, yq);
+        sh.ks[tid] = conv_out(c1, yk);
+        if (qk_owner && keep) {
+          conv_store(a, dslot, c0, yq);
+          conv_store(a, dslot, c1, yk);
+        }
+        conv_roll(c0, yq);
+        conv_roll(c1, yk);
+      } else if (v_thread) {
+        const float yv = sh.y[2][j];
+        sh.vs[j] = conv_out(c0, yv);
+        if (keep) conv_store(a, dslot, c0, yv);
+        conv_roll(c0, yv);
+      }
+      __syncthreads();
+      TRACE_POINT(2);
+      // One pass over the old state with the raw (not yet normalised) conv outputs k and q:
+      // per lane, the partial sums over its rows of S^T k and S^T q for its 4 columns and of
+      // k.k, q.q and k.q; then sums over the row groups by an xor butterfly inside the wave,
+      // after which every lane of a column quad holds the same totals.
+      float v[11] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-      const int i = rg + NRG * m;
-      const float k = sh.ks[i], q = sh.qs[i];
+      for (int m = 0; m < RPT; ++m) {
+        const int i = rg + NRG * m;
+        const float k = sh.ks[i], q = sh.qs[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[c] = fmaf(S[m][c], k, v[c]);
+          v[4 + c] = fmaf(S[m][c], q, v[4 + c]);
+        }
+        v[8] = fmaf(k, k, v[8]);
+        v[9] = fmaf(q, q, v[9]);
+        v[10] = fmaf(k, q, v[10]);
+      }
+#pragma unroll
+      for (int mask = QW; mask < 64; mask <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 11; ++e) v[e] += __shfl_xor(v[e], mask, 64);
+      }
+      TRACE_POINT(6);
+      const float kscale = 1.0f / sqrtf(v[8] + a.l2eps);                                   // 1 / |k|
+      const float qscale = (1.0f / sqrtf(v[9] + a.l2eps)) * (1.0f / sqrtf((float)DK));   // 1 / (|q| sqrt(dk))
+      const float decay = sh.scal[2], beta = sh.scal[3];
+      const float kq = v[10] * kscale * qscale;  // (normalised k) . (normalised, scaled q)
+      // With u = S^T k and w = S^T q of the old state, the updated state
+      // S' = e^g S + k d^T, d = beta (v - e^g u), reads out o = S'^T q = e^g w + d (k . q).
+      float d[4], ob[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        v[c] = fmaf(S[m][c], k, v[c]);
-        v[4 + c] = fmaf(S[m][c], q, v[4 + c]);
+        d[c] = beta * (sh.vs[4 * cq + c] - decay * (v[c] * kscale));
+        ob[c] = rbf(fmaf(d[c], kq, decay * (v[4 + c] * qscale)));
       }
-      v[8] = fmaf(k, k, v[8]);
-      v[9] = fmaf(q, q, v[9]);
-      v[10] = fmaf(k, q, v[10]);
-    }
+      // the state update and its stores go first; the gated norm needs a sum over all columns
 #pragma unroll
-    for (int mask = QW; mask < 64; mask <<= 1) {
+      for (int m = 0; m < RPT; ++m) {
+        const float kh = sh.ks[rg + NRG * m] * kscale;
 #pragma unroll
-      for (int e = 0; e < 11; ++e) v[e] += __shfl_xor(v[e], mask, 64);
-    }
-    TRACE_POINT(6);
-    const float kscale = 1.0f / sqrtf(v[8] + a.l2eps);                                   // 1 / |k|
-    const float qscale = (1.0f / sqrtf(v[9] + a.l2eps)) * (1.0f / sqrtf((float)DK));   // 1 / (|q| sqrt(dk))
-    const float decay = sh.scal[2], beta = sh.scal[3];
-    const float kq = v[10] * kscale * qscale;  // (normalised k) . (normalised, scaled q)
-    // With u = S^T k and w = S^T q of the old state, the updated state
-    // S' = e^g S + k d^T, d = beta (v - e^g u), reads out o = S'^T q = e^g w + d (k . q).
-    float d[4], ob[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      d[c] = beta * (sh.vs[4 * cq + c] - decay * (v[c] * kscale));
-      ob[c] = rbf(fmaf(d[c], kq, decay * (v[4 + c] * qscale)));
-    }
-    // the state update and its stores go first; the gated norm needs a sum over all columns
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-      const float kh = sh.ks[rg + NRG * m] * kscale;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) S[m][c] = fmaf(decay, S[m][c], kh * d[c]);
-      StateIO<ST>::store(a.ssm, sbase + (size_t)(rg + NRG * m) * DV, S[m]);
-    }
-    TRACE_POINT(7);
-    // RMSNormGated over the head: the lanes of row group 0 hold each column once
-    float ss = 0.0f;
-    if (rg == 0) ss = (ob[0] * ob[0] + ob[1] * ob[1]) + (ob[2] * ob[2] + ob[3] * ob[3]);
-    ss = block_sum(ss, sh.bsum);
-    const float rstd = 1.0f / sqrtf(ss / (float)DV + a.geps);
-    if (rg == 0) {
-      const float g0 = bf2f((uint16_t)gw4.x), g1 = bf2f((uint16_t)(gw4.x >> 16));
-      const float g2 = bf2f((uint16_t)gw4.y), g3 = bf2f((uint16_t)(gw4.y >> 16));
-      const float* z = &sh.y[3][4 * cq];
-      const uint64_t o = (uint64_t)f2bf2(ob[0] * rstd * g0 * silu(z[0]), ob[1] * rstd * g1 * silu(z[1])) |
-                         ((uint64_t)f2bf2(ob[2] * rstd * g2 * silu(z[2]), ob[3] * rstd * g3 * silu(z[3])) << 32);
-      uint64_t* dst = reinterpret_cast<uint64_t*>(core + 4 * cq);
-      if (a.fold)  // read by the out_proj workgroups: coherent at agent scope
-        __hip_atomic_store(dst, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else
-        *dst = o;
-    }
-    TRACE_POINT(3);
-
-    if (qk_owner) {
-      // the key head's other value heads have read the old q|k conv rows once they are counted
-      if (a.r > 1) wait_count(sy(a, sy_conv(a, n, kap)), (uint32_t)(a.r - 1), sy(a, kSyError), kErrConvWait);
-      if (qk_thread) {
-        conv_store(a, slot, c0, yq);
-        conv_store(a, slot, c1, yk);
+        for (int c = 0; c < 4; ++c) S[m][c] = fmaf(decay, S[m][c], kh * d[c]);
+        if (keep) StateIO<ST>::store(a.ssm, dslot * tile + hoff + (size_t)(rg + NRG * m) * DV, S[m]);
       }
-      if (tid == 0 && a.r > 1) st_agent(sy(a, sy_conv(a, n, kap)), 0u);
+      TRACE_POINT(7);
+      // RMSNormGated over the head: the lanes of row group 0 hold each column once
+      float ss = 0.0f;
+      if (rg == 0) ss = (ob[0] * ob[0] + ob[1] * ob[1]) + (ob[2] * ob[2] + ob[3] * ob[3]);
+      ss = block_sum(ss, sh.bsum);
+      const float rstd = 1.0f / sqrtf(ss / (float)DV + a.geps);
+      if (rg == 0) {
+        const float g0 = bf2f((uint16_t)gw4.x), g1 = bf2f((uint16_t)(gw4.x >> 16));
+        const float g2 = bf2f((uint16_t)gw4.y), g3 = bf2f((uint16_t)(gw4.y >> 16));
+        const float* z = &sh.y[3][4 * cq];
+        const uint64_t o = (uint64_t)f2bf2(ob[0] * rstd * g0 * silu(z[0]), ob[1] * rstd * g1 * silu(z[1])) |
+                           ((uint64_t)f2bf2(ob[2] * rstd * g2 * silu(z[2]), ob[3] * rstd * g3 * silu(z[3])) << 32);
+        uint64_t* dst = reinterpret_cast<uint64_t*>(a.core + (size_t)n * a.nv * DV + (size_t)h * DV + 4 * cq);
+        if (a.fold)  // read by the out_proj workgroups: coherent at agent scope
+          __hip_atomic_store(dst, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *dst = o;
+      }
+      TRACE_POINT(3);
     }
+    if (qk_owner && tid == 0 && a.r > 1) st_agent(sy(a, sy_conv(a, seq, kap)), 0u);
   } else {
     if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
-    // pad row: a zero core row
-    for (int j = 2 * tid; j < DV; j += 2 * kThreads) st_agent(reinterpret_cast<uint32_t*>(core + j), 0u);
+    // pad sequence: a zero core row for each of its tokens
+    for (int t = 0; t < Tk; ++t) {
+      uint16_t* core = a.core + (size_t)(seq * Tk + t) * a.nv * DV + (size_t)h * DV;
+      for (int j = 2 * tid; j < DV; j += 2 * kThreads) st_agent(reinterpret_cast<uint32_t*>(core + j), 0u);
+    }
   }
-  if (a.fold) {  // the core row of this head is in place for the out_proj workgroups
+  if (a.fold) {  // the core rows of this head are in place for the out_proj workgroups
     wait_stores();
     __syncthreads();
     if (tid < kCoreCopies) add_agent(sy(a, kSyCoreDone + tid), 1u);
@@ -1116,7 +1143,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   // by then every projection tile has been counted (each group and the b|a tiles had a
   // waiter), so every projection workgroup is past its norm wait, and no recurrence
   // workgroup reads a counter again (the q|k conv counter is cleared by its owner).
-  if (tid == 128 && exit_ticket == (uint32_t)(a.R * a.nv - 1)) {
+  if (tid == 128 && exit_ticket == (uint32_t)(a.Rs * a.nv - 1)) {
     // the norm workgroups may still be rewriting residual rows (past their last wait)
     int it = 0;
     while (ld_agent(sy(a, kSyNormExit)) < (uint32_t)(a.R * a.P) && ++it <= kSpinLimit) __builtin_amdgcn_s_sleep(4);
@@ -1153,7 +1180,7 @@ __device__ void oproj_role(const Args& a, int ob, ProjShared& sh) {
   for (int u = 0; u < kOutSteps; ++u)
     if (u < nsteps) w[u] = __builtin_nontemporal_load(wop(u));
 
-  wait_count(sy(a, kSyCoreDone + ob % kCoreCopies), (uint32_t)(a.R * a.nv), sy(a, kSyError), kErrGroupWait);
+  wait_count(sy(a, kSyCoreDone + ob % kCoreCopies), (uint32_t)(a.Rs * a.nv), sy(a, kSyError), kErrGroupWait);
   TRACE_POINT(1);
   // core rows [R, K] into LDS with direct-to-LDS loads, all in flight at once (plain
   // loads: first read after the count). One wave instruction fills 1 KiB of LDS, 16 bytes
@@ -1216,7 +1243,7 @@ __device__ void oproj_role(const Args& a, int ob, ProjShared& sh) {
 
 // FOLD is a template flag, not only a launch argument, so that the out_proj role's register
 // tile does not raise the register count (and lower the occupancy) of the launches without it.
-template <bool PACKED, int FMT, int DK, typename ST, bool FOLD>
+template <bool PACKED, int FMT, int DK, typename ST, bool FOLD, bool MULTI>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   __shared__ union {
     ProjShared proj;
@@ -1224,13 +1251,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   } sh;
   const int b = blockIdx.x;
   TRACE_POINT(0);
-  const int nn = a.R * a.P, nr = a.R * a.nv;
+  const int nn = a.R * a.P, nr = a.Rs * a.nv;
   if (b < nn) {
     norm_role<FMT == kFmtMx4>(a, b, sh.rec.bsum);
   } else if (b < nn + a.G) {
     proj_role<PACKED, FMT>(a, b - nn, sh.proj);
   } else if (b < nn + a.G + nr) {
-    rec_role<DK, ST>(a, b - nn - a.G, sh.rec);
+    rec_role<DK, ST, MULTI>(a, b - nn - a.G, sh.rec);
   } else if (FOLD) {
     oproj_role<PACKED>(a, b - nn - a.G - nr, sh.proj);
   }
@@ -1442,9 +1469,11 @@ int fail(gdn_block* b, int code, const std::string& msg) {
 template <bool PACKED, int FMT, int DK, typename ST>
 void launch_st(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
   if (b->fold)
-    hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, true>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, true, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  else if (a.dst)
+    hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, false, true>), dim3(grid), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, false>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, false, false>), dim3(grid), dim3(kThreads), 0, st, a);
 }
 
 template <bool PACKED, int FMT, int DK>
@@ -1609,13 +1638,19 @@ extern "C" int gdn_block_pack_weights(gdn_block_t b, const gdn_block_weights* w,
 }
 
 namespace {
+// one launch over `rows` sequences of `tokens` tokens each (decode: tokens = 1, dst_idx null)
 int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_weights* w, void* conv_state,
-                void* ssm_state, const int32_t* state_idx, int32_t rows, void* core_out, void* out, void* stream) {
+                void* ssm_state, const int32_t* state_idx, const int32_t* dst_idx, int32_t rows, int32_t tokens,
+                void* core_out, void* out, void* stream) {
   const gdn_block_config& c = b->cfg;
-  if (rows < 0 || rows > c.max_rows)
+  if (tokens < 1 || tokens > c.max_rows)
+    return fail(b, GDN_E_INVALID_ARG, "gdn_block_verify: tokens must be in 1.." + std::to_string(c.max_rows) +
+                                          " (got " + std::to_string(tokens) + ")");
+  if (rows < 0 || (long long)rows * tokens > c.max_rows)
     return fail(b, GDN_E_INVALID_ARG,
-                "gdn_block_decode: rows must be in 0.." + std::to_string(c.max_rows) + " (got " +
-                    std::to_string(rows) + ")");
+                std::string(tokens > 1 || dst_idx ? "gdn_block_verify: rows * tokens" : "gdn_block_decode: rows") +
+                    " must be in 0.." + std::to_string(c.max_rows) + " (got " + std::to_string(rows) +
+                    (tokens > 1 ? " x " + std::to_string(tokens) : std::string()) + ")");
   if (!w) return fail(b, GDN_E_INVALID_ARG, "gdn_block_decode: weights must not be NULL");
   if (b->fold) {
     if (!out || !aligned16(out))
@@ -1641,6 +1676,8 @@ int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_wei
     if (!aligned16(ptrs[i]))
       return fail(b, GDN_E_INVALID_ARG, std::string("gdn_block_decode: ") + names[i] + " is not 16-byte aligned");
   }
+  if (dst_idx && !aligned16(dst_idx))
+    return fail(b, GDN_E_INVALID_ARG, "gdn_block_verify: dst_idx is not 16-byte aligned");
   if (rows == 0) return GDN_OK;
 
   Args a;
@@ -1662,6 +1699,7 @@ int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_wei
   a.conv_state = static_cast<uint16_t*>(conv_state);
   a.ssm = ssm_state;
   a.idx = state_idx;
+  a.dst = dst_idx;
   a.A_log = w->A_log;
   a.dt_bias = static_cast<const uint16_t*>(w->dt_bias);
   a.gnw = static_cast<const uint16_t*>(w->gated_norm_w);
@@ -1680,7 +1718,9 @@ int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_wei
   a.part = b->part;
   a.sync = b->sync;
   a.H = c.hidden;
-  a.R = rows;
+  a.R = rows * tokens;
+  a.Rs = rows;
+  a.Tk = tokens;
   a.has_res = c.has_residual;
   a.normed = normed ? 1 : 0;
   a.P = normed ? 0 : (c.hidden / 8 + kThreads - 1) / kThreads;
@@ -1708,7 +1748,7 @@ int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_wei
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // no norm workgroups with a normed input; the out_proj workgroups last
-  const int grid = rows * a.P + a.G + rows * c.num_v_heads + a.O;
+  const int grid = a.R * a.P + a.G + rows * c.num_v_heads + a.O;
   if (packed)
     launch<true>(b, a, grid, st);
   else
@@ -1726,7 +1766,7 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   if (b->fold)
     return fail(b, GDN_E_INVALID_ARG,
                 "gdn_block_decode: this handle folds out_proj; call gdn_block_decode_with_out_proj");
-  return decode_impl(b, x, residual, w, conv_state, ssm_state, state_idx, rows, core_out, nullptr, stream);
+  return decode_impl(b, x, residual, w, conv_state, ssm_state, state_idx, nullptr, rows, 1, core_out, nullptr, stream);
 }
 
 extern "C" int gdn_block_decode_with_out_proj(gdn_block_t b, const void* x, void* residual, const gdn_block_weights* w,
@@ -1736,7 +1776,18 @@ extern "C" int gdn_block_decode_with_out_proj(gdn_block_t b, const void* x, void
   if (!b->fold)
     return fail(b, GDN_E_INVALID_ARG,
                 "gdn_block_decode_with_out_proj: this handle was created without fold_out_proj");
-  return decode_impl(b, x, residual, w, conv_state, ssm_state, state_idx, rows, core_out, out, stream);
+  return decode_impl(b, x, residual, w, conv_state, ssm_state, state_idx, nullptr, rows, 1, core_out, out, stream);
+}
+
+extern "C" int gdn_block_verify(gdn_block_t b, const void* x, void* residual, const gdn_block_weights* w,
+                                void* conv_state, void* ssm_state, const int32_t* src_idx, const int32_t* dst_idx,
+                                int32_t rows, int32_t tokens, void* core_out, void* stream) {
+  if (!b) return GDN_E_INVALID_ARG;
+  if (!dst_idx) return fail(b, GDN_E_INVALID_ARG, "gdn_block_verify: dst_idx must not be NULL");
+  if (b->fold)
+    return fail(b, GDN_E_INVALID_ARG, "gdn_block_verify: not for a handle that folds out_proj");
+  return decode_impl(b, x, residual, w, conv_state, ssm_state, src_idx, dst_idx, rows, tokens, core_out, nullptr,
+                     stream);
 }
 
 extern "C" int gdn_block_check(gdn_block_t b, uint32_t* error_word) {

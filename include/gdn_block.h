@@ -173,6 +173,26 @@ int gdn_block_decode_with_out_proj(gdn_block_t blk, const void* x, void* residua
                                    void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
                                    void* core_out, void* out, void* stream);
 
+/* One launch over `rows` sequences of `tokens` tokens each (a speculative-decoding verify
+ * step: the accepted token and its drafts), rows * tokens <= max_rows. Token t of sequence r
+ * is row r * tokens + t of x, residual and core_out ([rows * tokens, ...], as in decode).
+ * Each sequence starts from the state in slot src_idx[r] (device, [rows] int32) and runs
+ * its tokens one after the other, as that many decode steps would; after token t the SSM
+ * state and the conv window are stored into slot dst_idx[r * tokens + t] (device,
+ * [rows, tokens] int32, 16-byte aligned), unless that index is <= 0 or >= num_state_slots
+ * (then that snapshot is not kept). The source slot is only read, unless it is also one of
+ * the sequence's own destinations. A caller that accepts n tokens continues from
+ * dst_idx[r * tokens + n - 1]: a rejected draft leaves nothing to undo (the follow-up
+ * "sgl-amd-mono PR #89", Modifications, and "vLLM PR #60833", Limitations, leave open: K1
+ * keeps no state per draft token). A sequence with src_idx <= 0 (or >= num_state_slots) is
+ * a pad: zero core rows, no state read or written. Preconditions: the valid destination
+ * slots of a call are distinct and none is another sequence's source. With tokens == 1 and
+ * dst_idx[r] == src_idx[r] the results equal gdn_block_decode's, bit for bit. Not for a
+ * handle with fold_out_proj. Asynchronous, allocates nothing; errors as gdn_block_decode. */
+int gdn_block_verify(gdn_block_t blk, const void* x, void* residual, const gdn_block_weights* w,
+                     void* conv_state, void* ssm_state, const int32_t* src_idx, const int32_t* dst_idx,
+                     int32_t rows, int32_t tokens, void* core_out, void* stream);
+
 /* Size in bytes of the tiled projection copy (16-row tiles of [in_proj_qkvz;
  * in_proj_ba], the last b|a tile zero-padded): Nqkvz*H*2 (bf16), Nqkvz*H/2 +
  * Nqkvz*H/32 (MXFP4) or Nqkvz*H*3/4 + Nqkvz*H/32 (MXFP6), plus ceil(2*nv/16) * 16 * H * 2, plus H * nv*dv * 2 with
