@@ -130,6 +130,60 @@ class Rotation:
         torch.cuda.empty_cache()
 
 
+class VerifyRotation(Rotation):
+    """`layers` copies of a layer set up for verify steps of `seqs` sequences of `tokens`
+    tokens: every copy reads its sources and writes all of its snapshots into slots
+    disjoint from them, so every replay does the same work."""
+
+    def __init__(self, shape, layers, seqs, tokens, seed=0):
+        import numpy as np
+        import torch
+
+        from gated_deltanet_linear_decode_amd import synth
+        from gated_deltanet_linear_decode_amd.block import GdnBlock
+
+        dev = torch.device("cuda:0")
+        self.shape, self.dev, self.tokens = shape, dev, tokens
+        rows = seqs * tokens
+        self.blk = GdnBlock(shape, max_rows=rows, device=dev)
+        self.w_cpu = synth.make_weights(shape, seed)
+        self.call_cpu = synth.make_call(shape, rows, seed)
+        rng = np.random.Generator(np.random.PCG64(seed + 5))
+        perm = (rng.permutation(shape.num_state_slots - 1)[:seqs + rows] + 1).astype(np.int32)
+        src, dst = torch.from_numpy(perm[:seqs].copy()), torch.from_numpy(perm[seqs:].reshape(seqs, tokens).copy())
+        self.copies = []
+        for i in range(layers):
+            w = synth.GdnWeights(**{k: (v.to(dev).clone() if v is not None else None)
+                                    for k, v in self.w_cpu.__dict__.items()})
+            packed = self.blk.pack(w)
+            self.copies.append(dict(
+                w=w, ws=self.blk.weights_struct(w), packed=packed, wsp=self.blk.packed_struct(w, packed),
+                x=self.call_cpu.x.to(dev).clone(), res=self.call_cpu.residual.to(dev).clone(),
+                conv=self.call_cpu.conv_state.to(dev).clone(), ssm=self.call_cpu.ssm_state.to(dev).clone(),
+                src=src.to(dev), dst=dst.to(dev),
+                core=torch.empty(rows, shape.value_dim, dtype=torch.bfloat16, device=dev)))
+        torch.cuda.synchronize()
+
+    def launch(self, i, rows, packed):
+        c = self.copies[i % len(self.copies)]
+        self.blk.verify(c["x"], c["res"], None, c["conv"], c["ssm"], c["src"], c["dst"], c["core"],
+                        weights_struct=c["wsp"] if packed else c["ws"])
+
+
+def sweep_verify(shape, pairs, steps):
+    """µs per verify launch for each (sequences, tokens) pair."""
+    out = {}
+    for seqs, tokens in pairs:
+        rot = VerifyRotation(shape, shape.layers, seqs, tokens)
+        t = rot.time(seqs * tokens, steps, steps // 4)
+        b = configs_mod().algorithmic_bytes_verify(shape, seqs, tokens)
+        out[f"{seqs}x{tokens}"] = dict(us=round(t, 3), algo_bytes=b, gbs=round(b / (t * 1e-6) / 1e9, 1),
+                                       frac=round(b / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+        log(f"verify {shape.name} {seqs} sequences x {tokens} tokens: {t:.2f} us/launch")
+        rot.close()
+    return out
+
+
 def sweep_workload(shape, rows_list, steps, packed=True):
     """µs per launch of `shape` (its own layer count, pad rows as the workload has them)."""
     rot = Rotation(shape, shape.layers, max(rows_list), pads=shape.pad_rows)
@@ -200,6 +254,8 @@ def main():
     ap.add_argument("--workloads", default="tp8_rank_f32_state_pads,dense_full_width,tp8_rank_mxfp4,tp8_rank_mxfp6,"
                     "tp8_rank_bf16_state_normed_input,tp8_rank_mxfp4_normed_input,tp8_rank_bf16_state_out_proj",
                     help="other workloads to sweep (tiled weights) after the headline; '' for none")
+    ap.add_argument("--verify", default="1x2,1x4,2x4,4x4,8x2",
+                    help="verify steps (sequences x tokens) to time on the headline shape; '' for none")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -250,6 +306,9 @@ def main():
         log(f"sweeping {name}: rows {rows_list}, {wl.layers} layer copies")
         workloads[name] = sweep_workload(wl, rows_list, args.sweep_steps)
 
+    pairs = [tuple(int(v) for v in p.split("x")) for p in args.verify.split(",") if p]
+    verify = sweep_verify(shape, pairs, args.sweep_steps) if pairs else {}
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -291,6 +350,7 @@ def main():
         },
         "sweep": sweep,
         "workloads": workloads,
+        "verify": verify,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -180,3 +180,14 @@ def algorithmic_bytes(shape: GdnShape, rows: int, valid_rows: int | None = None)
     ssm_slot = ssm_elem * s.num_v_heads * s.head_k_dim * s.head_v_dim
     conv_slot = 2 * (s.conv_width - 1) * s.conv_dim
     return w_qkvz + w_other + rows * per_row + v * 2 * (ssm_slot + conv_slot)
+
+
+def algorithmic_bytes_verify(shape: GdnShape, seqs: int, tokens: int, kept: int | None = None) -> int:
+    """Bytes one verify launch must move: the weights once, every token row's input, residual
+    and core as in a decode row, each sequence's source state read once, and each kept
+    snapshot (the state and conv window after a token) written once."""
+    s = shape
+    ssm_elem = 4 if s.ssm_state_dtype == SSM_F32 else 2
+    slot = ssm_elem * s.num_v_heads * s.head_k_dim * s.head_v_dim + 2 * (s.conv_width - 1) * s.conv_dim
+    no_state = algorithmic_bytes(s, seqs * tokens, 0)
+    return no_state + seqs * slot + (seqs * tokens if kept is None else kept) * slot
