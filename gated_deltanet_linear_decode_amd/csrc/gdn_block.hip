@@ -77,13 +77,15 @@ constexpr int kThreads = 256;      // every role runs 4 waves of 64
 constexpr int kLine = 32;          // uint32 words per 128-byte line: one hot counter per line
 // Weight loads each wave keeps in flight (1 KiB each). The window is refilled as it is
 // consumed: enough bytes in flight to keep HBM busy, few enough that the hand-offs between
-// workgroups are not queued behind the whole weight matrix.
+// workgroups are not queued behind the whole weight matrix. Measured at the TP8-rank shape:
+// 8 beats 2, 4 and 6, and also 12, 16 and 24 (deeper windows slow the stream itself).
 #ifndef GDN_WINDOW
 #define GDN_WINDOW 8
 #endif
 constexpr int kWin = GDN_WINDOW;
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kNormCopies = 8;     // the norm-done counter is kept on 8 lines, polled spread out
+constexpr int kGroupCopies = 8;    // a key-head group's tiles-done counter is spread over 8 lines
 constexpr int kCoreCopies = 16;    // so is the core-done counter of the out_proj fold, on 16
 
 // ---------------------------------------------------------------------------------------
@@ -197,8 +199,8 @@ __device__ unsigned long long g_trace[kTraceBlocks * kTraceSlots];
 // polled spread out); b|a tile splits done; recurrence workgroups finished; the sticky
 // error word; norm workgroups finished; out_proj workgroups past their wait and (on
 // kCoreCopies lines) recurrence workgroups whose core rows are stored (out_proj fold);
-// then per key-head group: tile splits done; then per (row, key-head group): value heads
-// that have read the old q|k conv rows.
+// then per key-head group, on kGroupCopies lines: tile splits done; then per (sequence,
+// key-head group): value heads that have read the old q|k conv rows.
 enum {
   kSyNorm = 0,
   kSyBa = kNormCopies,
@@ -257,8 +259,10 @@ struct Args {
 };
 
 __device__ __forceinline__ uint32_t* sy(const Args& a, int line) { return a.sync + (size_t)line * kLine; }
-__device__ __forceinline__ int sy_group(int g) { return kSyGroup0 + g; }
-__device__ __forceinline__ int sy_conv(const Args& a, int n, int g) { return kSyGroup0 + a.nk + n * a.nk + g; }
+__device__ __forceinline__ int sy_group(int g, int c) { return kSyGroup0 + g * kGroupCopies + c; }
+__device__ __forceinline__ int sy_conv(const Args& a, int n, int g) {
+  return kSyGroup0 + a.nk * kGroupCopies + n * a.nk + g;
+}
 
 // ---------------------------------------------------------------------------------------
 // role 1: residual add + Gemma RMSNorm of one row
@@ -423,7 +427,7 @@ __device__ __forceinline__ void publish_reduced(const Args& a, int t, int s, f32
   if (en < a.R && (isq || ch < a.Nq + a.Nb)) st_agent(&a.part[((size_t)s * a.R + en) * (a.Nq + a.Nb) + ch], v);
   wait_stores();
   __syncthreads();
-  if (tid == 0) add_agent(sy(a, isq ? sy_group(t * 16 / a.GW) : kSyBa), 1u);
+  if (tid == 0) add_agent(sy(a, kSyBa), 1u);  // only b|a tiles are published this way
 }
 
 // each wave's own in_proj_qkvz tile -> its split partials; then the 4 tiles (one key-head
@@ -438,7 +442,33 @@ __device__ __forceinline__ void publish_tiles(const Args& a, int t0, int s, f32x
   }
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) add_agent(sy(a, sy_group(t0 * 16 / a.GW)), 1u);
+  // The group's tile workgroups count themselves on kGroupCopies lines (one line takes the
+  // atomics one at a time: ~96 arriving together would queue for about a microsecond).
+  // Workgroup li of the group (tile group, then split) counts on line li % kGroupCopies.
+  if (threadIdx.x == 0) {
+    const int g = t0 * 16 / a.GW, li = (t0 / 4 - g * (a.GW / 64)) * a.S + s;
+    add_agent(sy(a, sy_group(g, li % kGroupCopies)), 1u);
+  }
+}
+
+// waits until every tile workgroup of key-head group g has counted itself: lane c of the
+// first wave polls line c for its share, (n - c + C - 1) / C of the group's n workgroups
+__device__ __forceinline__ void wait_group(const Args& a, int g) {
+  if (threadIdx.x < 64) {
+    const int c = threadIdx.x, n = a.GW / 64 * a.S;
+    const int share = c < kGroupCopies ? max(0, (n - c + kGroupCopies - 1) / kGroupCopies) : 0;
+    uint32_t* ctr = sy(a, sy_group(g, c < kGroupCopies ? c : 0));
+    int it = 0;
+    while (!__all(share == 0 || ld_agent(ctr) >= (uint32_t)share)) {
+      __builtin_amdgcn_s_sleep(4);
+      if (++it > kSpinLimit) {
+        if (c == 0) __hip_atomic_fetch_or(sy(a, kSyError), kErrGroupWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  asm volatile("" ::: "memory");
 }
 
 // bf16 weight operand of K step j (32 wide) for this lane: 8 bf16 of row (lane % 16) at
@@ -1004,7 +1034,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   }
 
   // every recurrence workgroup waits, pad rows included (see the counter clearing below)
-  wait_count(sy(a, sy_group(kap)), (uint32_t)(a.GW / 64 * a.S), sy(a, kSyError), kErrGroupWait);
+  wait_group(a, kap);
   wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.S), sy(a, kSyError), kErrGroupWait);
   TRACE_POINT(1);
 
@@ -1151,7 +1181,8 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
     st_agent(sy(a, kSyNormExit), 0u);
     for (int c = 0; c < kNormCopies; ++c) st_agent(sy(a, kSyNorm + c), 0u);
     st_agent(sy(a, kSyBa), 0u);
-    for (int g = 0; g < a.nk; ++g) st_agent(sy(a, sy_group(g)), 0u);
+    for (int g = 0; g < a.nk; ++g)
+      for (int c = 0; c < kGroupCopies; ++c) st_agent(sy(a, sy_group(g, c)), 0u);
     st_agent(sy(a, kSyExit), 0u);
   }
   TRACE_POINT(4);
@@ -1540,7 +1571,7 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   b->kr = kr;
   const int S = H / kr;
   b->splits = S;
-  b->sync_words = (kSyGroup0 + nk + cfg->max_rows * nk) * kLine;
+  b->sync_words = (kSyGroup0 + nk * kGroupCopies + cfg->max_rows * nk) * kLine;
 
   const int R = cfg->max_rows;
   size_t off = 0;
