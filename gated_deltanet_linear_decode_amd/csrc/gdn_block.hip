@@ -885,7 +885,9 @@ struct StateIO<uint16_t> {
 };
 
 struct RecShared {
-  float y[4][128];                           // projection outputs q, k, v, z of the head (bf16 values)
+  float y[GDN_MAX_ROWS][4][128];             // per token: projection outputs q, k, v, z of the head (bf16
+                                             // values); a decode step uses token 0 only
+  float gt[GDN_MAX_ROWS][2];                 // verify: per token beta and exp(g)
   float qs[128], ks[128], vs[128];           // conv outputs q, k, v (SiLU, bf16 values)
   float scal[4];                             // [2] exp(g), [3] beta
   float bsum[4];
@@ -1043,37 +1045,73 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
     const int gbase = kap * a.GW;
     if (qk_owner && a.r > 1)  // the key head's other value heads have read the old q|k conv rows
       wait_count(sy(a, sy_conv(a, seq, kap)), (uint32_t)(a.r - 1), sy(a, kSyError), kErrConvWait);
+    // q | k | v | z channel of quad j (a multiple of 4) in block blk of the head's group
+    auto qch = [&](int blk, int j) {
+      return gbase + (blk == 0 ? j : blk == 1 ? DK + j : blk == 2 ? 2 * DK + hh * DV + j
+                                                      : 2 * DK + a.r * DV + hh * DV + j);
+    };
+    if constexpr (MULTI) {
+      // every token's projection outputs and gates first, 256 / DK tokens per pass, so the
+      // token loop below reads them from LDS instead of waiting for a load per token
+      constexpr int kTpp = kThreads / DK;
+#pragma unroll 1
+      for (int t0 = 0; t0 < Tk; t0 += kTpp) {
+        const int t = t0 + tid / DK, q = tid % DK;
+        if (t < Tk) {
+          const int blk = q / (DK / 4), j = 4 * (q % (DK / 4));
+          *reinterpret_cast<f32x4_t*>(&sh.y[t][blk][j]) = proj_quad(a, seq * Tk + t, qch(blk, j));
+        }
+      }
+      if (tid < 2 * Tk) {  // even threads b, odd threads a of token tid / 2
+        const int t = tid >> 1;
+        const float yg = proj_one(a, seq * Tk + t, a.Nq + kap * 2 * a.r + ((tid & 1) ? a.r : 0) + hh);
+        if (tid & 1) {
+          const float x = yg + dtb;
+          const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
+          sh.gt[t][1] = __expf(-__expf(alog) * sp);
+        } else {
+          sh.gt[t][0] = __builtin_amdgcn_rcpf(1.0f + __expf(-yg));
+        }
+      }
+      if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
+    }
 #pragma unroll 1
     for (int t = 0; t < Tk; ++t) {
       const int n = seq * Tk + t;  // the token's projection row
       const int dslot = MULTI ? a.dst[n] : slot;
       const bool keep = dslot > 0 && dslot < a.slots;  // store the state after this token
-      if (t > 0) __syncthreads();  // the previous token is done with the shared arrays
-      // threads < DK: one quad of the head's channels each, q | k | v | z in DK / 4 quads apiece
-      if (tid < DK) {
-        const int blk = tid / (DK / 4), j = 4 * (tid % (DK / 4));
-        const int ch = gbase + (blk == 0 ? j : blk == 1 ? DK + j : blk == 2 ? 2 * DK + hh * DV + j
-                                                                : 2 * DK + a.r * DV + hh * DV + j);
-        *reinterpret_cast<f32x4_t*>(&sh.y[blk][j]) = proj_quad(a, n, ch);
-      }
-      // the two gates are independent chains: thread 128 takes b, thread 192 takes a
-      float yg = 0.0f;
-      if (tid == 128 || tid == 192) yg = proj_one(a, n, a.Nq + kap * 2 * a.r + (tid == 192 ? a.r : 0) + hh);
-      // past every wait of this workgroup: count it (loads complete in issue order, so the
-      // atomic goes after this wave's loads to keep its latency off their path)
-      if (t == 0 && tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
-      TRACE_POINT(5);
-      if (tid == 128) {
-        sh.scal[3] = __builtin_amdgcn_rcpf(1.0f + __expf(-yg));  // beta = sigmoid(b)
-      } else if (tid == 192) {
-        const float x = yg + dtb;
-        const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
-        sh.scal[2] = __expf(-__expf(alog) * sp);  // exp(g), g = -exp(A_log) softplus(a + dt_bias)
+      if (MULTI || t > 0) __syncthreads();  // the previous token is done with the shared arrays
+      if constexpr (MULTI) {
+        if (tid == 0) {
+          sh.scal[3] = sh.gt[t][0];
+          sh.scal[2] = sh.gt[t][1];
+        }
+      } else {
+        // threads < DK: one quad of the head's channels each, q | k | v | z in DK / 4 quads apiece
+        if (tid < DK) {
+          const int blk = tid / (DK / 4), j = 4 * (tid % (DK / 4));
+          *reinterpret_cast<f32x4_t*>(&sh.y[0][blk][j]) = proj_quad(a, n, qch(blk, j));
+        }
+        // the two gates are independent chains: thread 128 takes b, thread 192 takes a
+        float yg = 0.0f;
+        if (tid == 128 || tid == 192) yg = proj_one(a, n, a.Nq + kap * 2 * a.r + (tid == 192 ? a.r : 0) + hh);
+        // past every wait of this workgroup: count it (loads complete in issue order, so the
+        // atomic goes after this wave's loads to keep its latency off their path)
+        if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
+        TRACE_POINT(5);
+        if (tid == 128) {
+          sh.scal[3] = __builtin_amdgcn_rcpf(1.0f + __expf(-yg));  // beta = sigmoid(b)
+        } else if (tid == 192) {
+          const float x = yg + dtb;
+          const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
+          sh.scal[2] = __expf(-__expf(alog) * sp);  // exp(g), g = -exp(A_log) softplus(a + dt_bias)
+        }
       }
       __syncthreads();
+      const int ty = MULTI ? t : 0;
       const int j = tid - 128;
       if (qk_thread) {
-        const float yq = sh.y[0][tid], yk = sh.y[1][tid];
+        const float yq = sh.y[ty][0][tid], yk = sh.y[ty][1][tid];
         sh.qs[tid] = conv_out(c0, yq);
         sh.ks[tid] = conv_out(c1, yk);
         if (qk_owner && keep) {
@@ -1083,7 +1121,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
         conv_roll(c0, yq);
         conv_roll(c1, yk);
       } else if (v_thread) {
-        const float yv = sh.y[2][j];
+        const float yv = sh.y[ty][2][j];
         sh.vs[j] = conv_out(c0, yv);
         if (keep) conv_store(a, dslot, c0, yv);
         conv_roll(c0, yv);
@@ -1143,7 +1181,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
       if (rg == 0) {
         const float g0 = bf2f((uint16_t)gw4.x), g1 = bf2f((uint16_t)(gw4.x >> 16));
         const float g2 = bf2f((uint16_t)gw4.y), g3 = bf2f((uint16_t)(gw4.y >> 16));
-        const float* z = &sh.y[3][4 * cq];
+        const float* z = &sh.y[ty][3][4 * cq];
         const uint64_t o = (uint64_t)f2bf2(ob[0] * rstd * g0 * silu(z[0]), ob[1] * rstd * g1 * silu(z[1])) |
                            ((uint64_t)f2bf2(ob[2] * rstd * g2 * silu(z[2]), ob[3] * rstd * g3 * silu(z[3])) << 32);
         uint64_t* dst = reinterpret_cast<uint64_t*>(a.core + (size_t)n * a.nv * DV + (size_t)h * DV + 4 * cq);
