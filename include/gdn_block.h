@@ -229,8 +229,9 @@ int gdn_mxfp6_round_weights(const void* w, int32_t rows, int32_t cols, void* cod
 /* Read and clear the handle's sticky error word (synchronous; not for the hot
  * path). Inside a decode, every wait for another workgroup is bounded; a wait
  * that gives up sets a bit (1: waiting for the norm rows, 2: waiting for a
- * key-head group's projection tiles) and lets the launch finish with undefined
- * outputs. 0 means every decode since the last check completed normally. */
+ * key-head group's projection tiles or, with fold_out_proj, for the core rows, 4:
+ * waiting for the other value heads of a key head to read its old q|k conv rows) and
+ * lets the launch finish with undefined outputs. 0 means every decode since the last check completed normally. */
 int gdn_block_check(gdn_block_t blk, uint32_t* error_word);
 
 /* Free the handle and its scratch (NULL is a no-op). Waits for nothing: the

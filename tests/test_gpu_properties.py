@@ -141,6 +141,83 @@ def test_graph_replay_equals_eager():
     blk.close()
 
 
+def test_graph_replay_fold_and_verify():
+    """One graph mixing out_proj-fold decodes (8 and 1 rows) and verify steps (2 x 4 and 1 x 3
+    tokens) on two handles, replayed 60 times: every replay equals the eager run bit for bit
+    (the fold's and verify's counters are cleared by the launches themselves)."""
+    import numpy as np
+    fold_shape = configs.TP8_RANK_BF16_OUT.with_(num_state_slots=48, rows=(8,))
+    ver_shape = configs.TP8_RANK_BF16.with_(num_state_slots=48, rows=(8,))
+    wf = weights_to(synth.make_weights(fold_shape, 25), DEV)
+    wv = weights_to(synth.make_weights(ver_shape, 25), DEV)
+    bf = GdnBlock(fold_shape, max_rows=8, device=DEV)
+    bv = GdnBlock(ver_shape, max_rows=8, device=DEV)
+    wsf, wsv = bf.packed_struct(wf, bf.pack(wf)), bv.packed_struct(wv, bv.pack(wv))
+    dcalls = [call_to(synth.make_call(fold_shape, r, 400 + r), DEV) for r in (8, 1)]
+    vcalls = [call_to(synth.make_call(ver_shape, s_ * t, 410 + t), DEV) for s_, t in ((2, 4), (1, 3))]
+    src = [torch.tensor([3, 7], dtype=torch.int32, device=DEV), torch.tensor([11], dtype=torch.int32, device=DEV)]
+    dst = [torch.tensor([[20, 21, 22, 3], [23, 0, 24, 25]], dtype=torch.int32, device=DEV),
+           torch.tensor([[30, 31, 32]], dtype=torch.int32, device=DEV)]
+    conv0f, ssm0f = dcalls[0].conv_state.clone(), dcalls[0].ssm_state.clone()
+    conv0v, ssm0v = vcalls[0].conv_state.clone(), vcalls[0].ssm_state.clone()
+    convf, ssmf, convv, ssmv = conv0f.clone(), ssm0f.clone(), conv0v.clone(), ssm0v.clone()
+    resd = [c.residual.clone() for c in dcalls]
+    resv = [c.residual.clone() for c in vcalls]
+    cored = [torch.zeros(c.x.shape[0], fold_shape.value_dim, dtype=torch.bfloat16, device=DEV) for c in dcalls]
+    outs = [torch.zeros(c.x.shape[0], fold_shape.hidden, dtype=torch.bfloat16, device=DEV) for c in dcalls]
+    corev = [torch.zeros(c.x.shape[0], ver_shape.value_dim, dtype=torch.bfloat16, device=DEV) for c in vcalls]
+
+    def step_all():
+        for i in range(2):
+            bf.decode(dcalls[i].x, resd[i], None, convf, ssmf, dcalls[i].state_idx, cored[i], weights_struct=wsf,
+                      out=outs[i])
+            bv.verify(vcalls[i].x, resv[i], None, convv, ssmv, src[i], dst[i], corev[i], weights_struct=wsv)
+
+    def reset():
+        convf.copy_(conv0f)
+        ssmf.copy_(ssm0f)
+        convv.copy_(conv0v)
+        ssmv.copy_(ssm0v)
+        for i in range(2):
+            resd[i].copy_(dcalls[i].residual)
+            resv[i].copy_(vcalls[i].residual)
+
+    def state():
+        return [convf, ssmf, convv, ssmv] + resd + resv + cored + outs + corev
+
+    reset()
+    step_all()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in state()]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        reset()
+        step_all()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step_all()
+    mismatches = 0
+    for rep in range(60):
+        reset()
+        for t in cored + outs + corev:
+            t.fill_(1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, state()):
+            bits = (lambda t: t.view(torch.int16)) if a.dtype == torch.bfloat16 else (lambda t: t)
+            if not torch.equal(bits(a), bits(b)):
+                mismatches += 1
+        if rep % 20 == 0:
+            note(f"fold/verify graph replay {rep}: mismatches so far {mismatches}")
+    assert mismatches == 0
+    assert bf.check() == 0 and bv.check() == 0
+    bf.close()
+    bv.close()
+
+
 def test_decode_rejects_bad_arguments_on_the_host():
     shape = configs.TINY
     w = weights_to(synth.make_weights(shape, 25), DEV)
