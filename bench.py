@@ -203,15 +203,21 @@ def configs_mod():
     return configs
 
 
-def cpu_baseline(shape, rot, rows, seconds):
-    """The oracle on the same workload (same bytes), timed for about `seconds`."""
+def cpu_baseline(shape, rot, rows, seconds, single_thread=False):
+    """The oracle on the same workload (same bytes), timed for about `seconds`, on all the
+    BLAS threads numpy has, or on one."""
+    import contextlib
+
     import numpy as np
     import torch
 
     import oracle
+    limit = contextlib.nullcontext()
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        if single_thread:
+            limit, threads = threadpool_limits(limits=1), 1
     except Exception:
         threads = 1
     bits = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16).copy()  # noqa: E731
@@ -227,15 +233,16 @@ def cpu_baseline(shape, rot, rows, seconds):
     ssm = bits(c.ssm_state) if c.ssm_state.dtype == torch.bfloat16 else c.ssm_state.numpy()
     idx = c.state_idx[:rows].numpy()
     n, t0 = 0, time.perf_counter()
-    while True:
-        oracle.decode_block(cfg, w, x, res, conv, ssm, idx)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    with limit:
+        while True:
+            oracle.decode_block(cfg, w, x, res, conv, ssm, idx)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
     return dict(value=el / n * 1e6, unit="µs/launch", cores=threads, kind="oracle",
                 sample=f"{n} oracle decode calls of the {rows}-row step of {shape.name} "
-                       f"(float64 numpy, {threads} BLAS threads), {el:.1f} s")
+                       f"(float64 numpy, {threads} BLAS thread{"s" if threads != 1 else ""}), {el:.1f} s")
 
 
 def main():
@@ -317,10 +324,11 @@ def main():
         if tr.get("kernel_source_hash") == kernel_source_hash() and entry:
             traffic = entry["bytes_per_launch"]
 
-    cpu = None
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
+        log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s, then on one thread")
         cpu = cpu_baseline(shape, rot, args.rows, args.cpu_seconds)
+        cpu1 = cpu_baseline(shape, rot, args.rows, args.cpu_seconds / 2, single_thread=True)
 
     out = {
         "metric": METRIC,
@@ -352,6 +360,7 @@ def main():
         "workloads": workloads,
         "verify": verify,
         "cpu_baseline": cpu,
+        "cpu_baseline_single_thread": cpu1,
     }
     print(json.dumps(out), flush=True)
 
