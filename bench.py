@@ -242,7 +242,7 @@ def cpu_baseline(shape, rot, rows, seconds, single_thread=False):
                 break
     return dict(value=el / n * 1e6, unit="µs/launch", cores=threads, kind="oracle",
                 sample=f"{n} oracle decode calls of the {rows}-row step of {shape.name} "
-                       f"(float64 numpy, {threads} BLAS thread{"s" if threads != 1 else ""}), {el:.1f} s")
+                       f"(float64 numpy, {threads} BLAS thread{'s' if threads != 1 else ''}), {el:.1f} s")
 
 
 def main():
