@@ -1,41 +1,47 @@
 // Gated DeltaNet decode block for gfx950: one fused decode kernel and the C ABI of
 // include/gdn_block.h.
 //
-// A decode call is ONE launch whose workgroups take one of three roles by block id
+// A decode call is ONE launch whose workgroups take one of four roles by block id
 // (the front of a GDN layer as one launch, "sgl-amd-mono PR #89", Modifications; the
 // "GDN block" of "vLLM PR #60833", Details / Launches):
 //
-//   [0, R*P)          norm: P = ceil(H / 2048) workgroups per row. Each loads the whole row,
-//                     forms h = bf16(x + residual) and the row's rstd (all P in the same
-//                     order, so with the same result), and publishes one 2048-wide slice of
-//                     xn = bf16(h * rstd * (1 + w)) to scratch; then it counts itself done
-//                     and rewrites its slice of the residual row with h (with a residual
-//                     input, once every norm workgroup has loaded its row). No workgroup
-//                     holds x in LDS; every projection workgroup reads the finished xn
-//                     ("vLLM PR #60833", Details / x without an LDS tile).
-//                     With MXFP4 in_proj_qkvz the slice is also quantised to MXFP4 (codes +
-//                     one e8m0 scale per 32) into a second scratch image.
+//   [0, R*P)          norm: P = ceil(H / 2048) workgroups per row (none when x is already
+//                     normed). Each loads the whole row, forms h = bf16(x + residual) and
+//                     the row's rstd (all P in the same order, so with the same result), and
+//                     publishes one 2048-wide slice of xn = bf16(h * rstd * (1 + w)) to
+//                     scratch; then it counts itself done and rewrites its slice of the
+//                     residual row with h (with a residual input, once every norm workgroup
+//                     has loaded its row). No workgroup holds x in LDS; every projection
+//                     workgroup reads the finished xn ("vLLM PR #60833", Details / x without
+//                     an LDS tile). With MXFP4 in_proj_qkvz the slice is also quantised to
+//                     MXFP4 (codes + one e8m0 scale per 32) into a second scratch image.
 //   [R*P, R*P+G)      projection: in_proj_qkvz and in_proj_ba as one skinny GEMM on the
 //                     matrix cores: bf16 weights on v_mfma_f32_16x16x32_bf16, MXFP4 weights
 //                     on v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 x fp4 with per-32 scales),
 //                     MXFP6 E2M3 weights converted to bf16 in registers (exactly) and then
 //                     on the bf16 instruction with the bf16 activations;
-//                     16 weight rows x 16 decode rows per instruction. Each workgroup owns
-//                     one 16-channel tile and one split of K. It issues its weight loads
-//                     first, then waits for the norm rows, multiplies, and publishes its f32
-//                     partial sums; then it counts itself done for the tile's key-head group
-//                     (or for the b|a tiles).
-//   [R*P+G, +R*nv)    recurrence: one workgroup per (row, value head). It loads its
+//                     16 weight rows x 16 decode rows per instruction. A workgroup owns one
+//                     K range and 4 in_proj_qkvz tiles (one per wave) or one in_proj_ba tile.
+//                     It issues its weight loads first, then waits for the norm rows, stages
+//                     the activations of its K range in LDS once, multiplies, and publishes
+//                     its f32 partial sums; then it counts itself done for the tiles'
+//                     key-head group (or for the b|a tiles).
+//   [.., +Rs*nv)      recurrence: one workgroup per (sequence, value head); a decode call
+//                     has one token per sequence, a verify call several. It loads its
 //                     dk x dv state tile and its conv state and taps first, waits for its
 //                     key-head group and the b|a tiles, adds the split partials of its
 //                     channels in split order and rounds them to bf16 (the projection
 //                     output), runs the causal conv update + SiLU, L2 norms, gates, the gated
-//                     delta rule, the state store and the gated RMSNorm into the core output.
-//                     The q|k conv state of a key head is shared by its r value heads: the
-//                     last of them writes it once the others have read the old rows.
+//                     delta rule, the state store and the gated RMSNorm into the core output,
+//                     token after token. The q|k conv state of a key head is shared by its r
+//                     value heads: the last of them writes it once the others have read the
+//                     old rows.
+//   [.., +H/64)       out_proj (folded in, optional): 4 tiles of 16 hidden columns per
+//                     workgroup; the weights stream from launch start, the core rows are
+//                     multiplied once every recurrence workgroup has stored its row.
 //
-// Every wait ends: projection and recurrence workgroups wait only for workgroups with
-// lower block ids, which the dispatcher starts first, and a norm workgroup's one wait
+// Every wait ends: projection, recurrence and out_proj workgroups wait only for workgroups
+// with lower block ids, which the dispatcher starts first, and a norm workgroup's one wait
 // (before its residual rewrite) is for the other norm workgroups, which count themselves
 // before they wait for anything. Each wait is also bounded and records a sticky error
 // word if it gives up. Data handed from one workgroup to another travels as agent-scope atomic
