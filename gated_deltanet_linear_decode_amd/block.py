@@ -95,7 +95,8 @@ class GdnBlock:
         return out
 
     def packed_struct(self, w, packed: torch.Tensor) -> abi.GdnBlockWeights:
-        """Weights struct that streams `packed` (from pack()) for the projections."""
+        """Weights struct that streams `packed` (from pack()) for the projections. The struct
+        holds raw device pointers: keep `packed` (and the weights) alive while it is used."""
         st = self.weights_struct(w)
         _check(packed, "packed", torch.uint8, (abi.gdn_block_packed_weight_bytes(self.handle),), self.device)
         st.w_proj_packed = packed.data_ptr()

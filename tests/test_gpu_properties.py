@@ -152,7 +152,8 @@ def test_graph_replay_fold_and_verify():
     wv = weights_to(synth.make_weights(ver_shape, 25), DEV)
     bf = GdnBlock(fold_shape, max_rows=8, device=DEV)
     bv = GdnBlock(ver_shape, max_rows=8, device=DEV)
-    wsf, wsv = bf.packed_struct(wf, bf.pack(wf)), bv.packed_struct(wv, bv.pack(wv))
+    packed_f, packed_v = bf.pack(wf), bv.pack(wv)  # kept alive: the structs hold raw pointers
+    wsf, wsv = bf.packed_struct(wf, packed_f), bv.packed_struct(wv, packed_v)
     dcalls = [call_to(synth.make_call(fold_shape, r, 400 + r), DEV) for r in (8, 1)]
     vcalls = [call_to(synth.make_call(ver_shape, s_ * t, 410 + t), DEV) for s_, t in ((2, 4), (1, 3))]
     src = [torch.tensor([3, 7], dtype=torch.int32, device=DEV), torch.tensor([11], dtype=torch.int32, device=DEV)]
@@ -185,6 +186,10 @@ def test_graph_replay_fold_and_verify():
     def state():
         return [convf, ssmf, convv, ssmv] + resd + resv + cored + outs + corev
 
+    names = ["conv fold", "ssm fold", "conv verify", "ssm verify", "residual fold 8", "residual fold 1",
+             "residual verify 2x4", "residual verify 1x3", "core fold 8", "core fold 1", "out fold 8",
+             "out fold 1", "core verify 2x4", "core verify 1x3"]
+
     reset()
     step_all()
     torch.cuda.synchronize()
@@ -206,10 +211,12 @@ def test_graph_replay_fold_and_verify():
             t.fill_(1.0)
         g.replay()
         torch.cuda.synchronize()
-        for a, b in zip(eager, state()):
+        for name, a, b in zip(names, eager, state()):
             bits = (lambda t: t.view(torch.int16)) if a.dtype == torch.bfloat16 else (lambda t: t)
             if not torch.equal(bits(a), bits(b)):
                 mismatches += 1
+                if rep == 0:
+                    note(f"  replay 0: {name} differs from the eager run")
         if rep % 20 == 0:
             note(f"fold/verify graph replay {rep}: mismatches so far {mismatches}")
     assert mismatches == 0
