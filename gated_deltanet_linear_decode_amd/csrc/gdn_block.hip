@@ -843,6 +843,12 @@ __device__ void proj_mx6(const Args& a, int gb, int t0, int s, ProjShared& sh) {
 // ranges each
 template <bool PACKED, int FMT>
 __device__ void proj_role(const Args& a, int gb, ProjShared& sh) {
+  // With MXFP4 weights (13.4 MB at the TP8-rank shape) the launch is bound by the norm
+  // hand-off rather than by the weight stream: holding the projection workgroups' first
+  // weight loads back by ~0.3 us lets the norm rows' loads through first. Measured at the
+  // TP8-rank shape: 0.35-0.5 us faster at 1-8 rows, 0.05-0.1 us slower at 12-16 rows; with
+  // bf16 or MXFP6 weights any delay costs time (the stream is the critical path there).
+  if (FMT == kFmtMx4 && !a.normed && a.R <= 8) __builtin_amdgcn_s_sleep(10);
   if (gb < a.Gq) {
     const int tg = gb / a.S, s = gb - tg * a.S;
     if (FMT == kFmtMx4)
