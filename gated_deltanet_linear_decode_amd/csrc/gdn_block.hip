@@ -649,15 +649,24 @@ struct MxUnit {
   uint32_t sc;   // the 4 steps' scales of this lane's row and K quarter
 };
 
+// Block b (1 KiB of codes, or 256 B of scales) of tile t in the tiled MXFP4 / MXFP6 copies,
+// grouped like the bf16 tiles (see wptr): [K range][group of 4 tiles][block of the range]
+// [tile of the group], with nb blocks per K range.
+__device__ __forceinline__ size_t mx_block(const Args& a, int t, int b, int nb) {
+  const int s = b / nb, bb = b - s * nb;
+  return (((size_t)s * (a.Tq >> 2) + (t >> 2)) * nb + bb) * 4 + (t & 3);
+}
+
 template <bool PACKED>
 __device__ __forceinline__ void mx_wload(const Args& a, int t, int U, int lane, MxUnit& m) {
   const int kb = lane >> 4;
   if (PACKED) {
-    const u32x4_t* c = reinterpret_cast<const u32x4_t*>(
-        reinterpret_cast<const uint8_t*>(a.wpk) + (((size_t)t * (a.steps >> 2) + 4 * U) * 64 + lane) * 16);
+    const int ns = a.Kr >> 7;  // 128-wide steps per K range
 #pragma unroll
-    for (int st = 0; st < 4; ++st) m.c[st] = __builtin_nontemporal_load(c + 64 * st);
-    m.sc = __builtin_nontemporal_load(a.wpk_sc + ((size_t)t * (a.steps >> 4) + U) * 64 + lane);
+    for (int st = 0; st < 4; ++st)
+      m.c[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+          reinterpret_cast<const uint8_t*>(a.wpk) + (mx_block(a, t, 4 * U + st, ns) * 64 + lane) * 16));
+    m.sc = __builtin_nontemporal_load(a.wpk_sc + mx_block(a, t, U, a.Kr >> 9) * 64 + lane);
   } else {
     const int row = t * 16 + (lane & 15);
     const uint8_t* c = a.wqc + (size_t)row * (a.H >> 1) + 256 * U + 16 * kb;
@@ -772,13 +781,14 @@ template <bool PACKED>
 __device__ __forceinline__ void mx6_wload(const Args& a, int t, int G, int lane, Mx6Group& m) {
   if (PACKED) {
     // a unit is 1.5 KiB: the 64 lanes' 16-byte parts, then their 8-byte parts
-    const uint8_t* u0 = reinterpret_cast<const uint8_t*>(a.wpk) + ((size_t)t * (a.H >> 7) + 4 * G) * 1536;
+    const int nu = a.Kr >> 7;  // units per K range
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      m.lo[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(u0 + u * 1536 + 16 * lane));
-      m.hi[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(u0 + u * 1536 + 1024 + 8 * lane));
+      const uint8_t* u0 = reinterpret_cast<const uint8_t*>(a.wpk) + mx_block(a, t, 4 * G + u, nu) * 1536;
+      m.lo[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(u0 + 16 * lane));
+      m.hi[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(u0 + 1024 + 8 * lane));
     }
-    m.sc = __builtin_nontemporal_load(a.wpk_sc + ((size_t)t * (a.H >> 9) + G) * 64 + lane);
+    m.sc = __builtin_nontemporal_load(a.wpk_sc + mx_block(a, t, G, a.Kr >> 9) * 64 + lane);
   } else {
     // row-major codes [Nq, H/32, 24]: block 16 G + 4 u + kb of the row is unit u's
     const int row = t * 16 + (lane & 15), kb = lane >> 4;
@@ -1374,35 +1384,41 @@ __global__ __launch_bounds__(64) void pack_kernel(const uint16_t* __restrict__ w
 
 // tiled copy of MXFP4 in_proj_qkvz codes: block (t, j) = 64 lanes x 16 bytes, lane l holding
 // the 32 codes of row 16 t + l % 16 at k = 128 j + 32 (l / 16)
+// index of block b of tile t when each K range holds nb blocks, grouped as
+// [K range][group of 4 tiles][block of the range][tile of the group] (Tq tiles in all)
+__device__ __forceinline__ size_t grouped_block(int t, int b, int nb, int Tq) {
+  const int s = b / nb, bb = b - s * nb;
+  return (((size_t)s * (Tq >> 2) + (t >> 2)) * nb + bb) * 4 + (t & 3);
+}
 __global__ __launch_bounds__(64) void pack_mx_codes_kernel(const uint8_t* __restrict__ wq, uint8_t* __restrict__ out,
-                                                           int H) {
+                                                           int H, int Tq, int kr) {
   const int j = blockIdx.x, t = blockIdx.y, l = threadIdx.x, row = t * 16 + (l & 15);
   const uint4 v = *reinterpret_cast<const uint4*>(wq + (size_t)row * (H >> 1) + 64 * j + 16 * (l >> 4));
-  *reinterpret_cast<uint4*>(out + (((size_t)t * (H >> 7) + j) * 64 + l) * 16) = v;
+  *reinterpret_cast<uint4*>(out + (grouped_block(t, j, kr >> 7, Tq) * 64 + l) * 16) = v;
 }
 
 // tiled copy of MXFP4 in_proj_qkvz scales: block (t, U) = 64 lanes x 4 bytes, lane l's byte
 // st holding the scale of row 16 t + l % 16, K step 4 U + st, quarter l / 16
 __global__ __launch_bounds__(64) void pack_mx_scales_kernel(const uint8_t* __restrict__ ws, uint32_t* __restrict__ out,
-                                                            int H) {
+                                                            int H, int Tq, int kr) {
   const int U = blockIdx.x, t = blockIdx.y, l = threadIdx.x, row = t * 16 + (l & 15), kb = l >> 4;
   const uint8_t* src = ws + (size_t)row * (H >> 5) + 16 * U;
   uint32_t d = 0;
 #pragma unroll
   for (int st = 0; st < 4; ++st) d |= (uint32_t)src[4 * st + kb] << (8 * st);
-  out[((size_t)t * (H >> 9) + U) * 64 + l] = d;
+  out[grouped_block(t, U, kr >> 9, Tq) * 64 + l] = d;
 }
 
 // tiled copy of MXFP6 in_proj_qkvz codes: unit (t, U) = 1.5 KiB, the 16-byte heads of the 64
 // lanes' code runs, then their 8-byte tails; lane l holding the 32 codes (24 bytes) of row
 // 16 t + l % 16 at k = 128 U + 32 (l / 16). The scales take the MXFP4 scale tiles' layout.
 __global__ __launch_bounds__(64) void pack_mx6_codes_kernel(const uint8_t* __restrict__ wq, uint8_t* __restrict__ out,
-                                                            int H) {
+                                                            int H, int Tq, int kr) {
   const int U = blockIdx.x, t = blockIdx.y, l = threadIdx.x, row = t * 16 + (l & 15);
   const uint8_t* src = wq + ((size_t)row * (H >> 5) + 4 * U + (l >> 4)) * 24;
   const u32x2_t p0 = *reinterpret_cast<const u32x2_t*>(src), p1 = *reinterpret_cast<const u32x2_t*>(src + 8);
   const u32x2_t p2 = *reinterpret_cast<const u32x2_t*>(src + 16);
-  uint8_t* dst = out + ((size_t)t * (H >> 7) + U) * 1536;
+  uint8_t* dst = out + grouped_block(t, U, kr >> 7, Tq) * 1536;
   *reinterpret_cast<u32x4_t*>(dst + 16 * l) = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
   *reinterpret_cast<u32x2_t*>(dst + 1024 + 8 * l) = p2;
 }
@@ -1714,12 +1730,12 @@ extern "C" int gdn_block_pack_weights(gdn_block_t b, const gdn_block_weights* w,
   } else {
     const uint8_t* codes = static_cast<const uint8_t*>(w->w_qkvz);
     if (b->fmt == kFmtMx4)
-      hipLaunchKernelGGL(pack_mx_codes_kernel, dim3(H / 128, b->tq), dim3(64), 0, st, codes, out, H);
+      hipLaunchKernelGGL(pack_mx_codes_kernel, dim3(H / 128, b->tq), dim3(64), 0, st, codes, out, H, b->tq, b->kr);
     else
-      hipLaunchKernelGGL(pack_mx6_codes_kernel, dim3(H / 128, b->tq), dim3(64), 0, st, codes, out, H);
+      hipLaunchKernelGGL(pack_mx6_codes_kernel, dim3(H / 128, b->tq), dim3(64), 0, st, codes, out, H, b->tq, b->kr);
     hipLaunchKernelGGL(pack_mx_scales_kernel, dim3(H / 512, b->tq), dim3(64), 0, st,
                        static_cast<const uint8_t*>(w->w_qkvz_scales),
-                       reinterpret_cast<uint32_t*>(out + packed_qkvz_bytes(b)), H);
+                       reinterpret_cast<uint32_t*>(out + packed_qkvz_bytes(b)), H, b->tq, b->kr);
     // the b|a tiles in the bf16 tile layout (pack_kernel with no in_proj_qkvz tiles)
     hipLaunchKernelGGL(pack_kernel, dim3(b->steps, b->tb), dim3(64), 0, st, static_cast<const uint16_t*>(w->w_ba),
                        static_cast<const uint16_t*>(w->w_ba), out_ba, H, 0, 0, b->nb, 0);

@@ -56,8 +56,8 @@
  * 1 KiB blocks in the operand order of the matrix cores, so every load instruction of
  * the projection reads 1 KiB of contiguous memory: bf16 tiles in 32-wide steps (the
  * in_proj_qkvz blocks ordered [K range][group of 4 tiles][step][tile], so a projection
- * workgroup's share is one contiguous run; in_proj_ba tiles one run per tile); MXFP4 code
- * tiles in 128-wide steps, followed by their scales, one
+ * workgroup's share is one contiguous run, and so are the MXFP4 / MXFP6 code and scale
+ * blocks below; in_proj_ba tiles one run per tile); MXFP4 code tiles in 128-wide steps, followed by their scales, one
  * dword per lane per 4 steps; MXFP6 tiles in 128-wide steps of 1.5 KiB (each lane's
  * 24 code bytes split as 16 + 8, the 16-byte parts of the 64 lanes first), followed by
  * their scales like MXFP4's. Pass it as w_proj_packed; w_qkvz, w_qkvz_scales and w_ba
