@@ -599,9 +599,12 @@ __device__ void proj_bf16(const Args& a, int gb, int t0, int s, ProjShared& sh) 
   const int t = TILES ? t0 + wave : t0;
   const int nsteps = TILES ? a.Kr >> 5 : a.Kr >> 7;
   const int l0 = TILES ? 0 : wave * nsteps;  // first local K step (32 wide) of this wave
-  // Each wave starts at its own point of its K range (a function of the tile and split
-  // only), so that the waves streaming at the same moment spread over the HBM channels.
-  const int rot = (t * 7 + s * 3 + wave) % nsteps;
+  // The 4 in_proj_qkvz tile waves of a workgroup step through their K range together, so
+  // that at each step they read 4 adjacent blocks of the grouped tiled copy (see wptr;
+  // measured faster than starting each wave at its own point of the range). The in_proj_ba
+  // waves each start at their own point, so that the waves streaming at the same moment
+  // spread over the HBM channels (a function of the tile and split only).
+  const int rot = TILES ? 0 : (t * 7 + s * 3 + wave) % nsteps;
   auto lstep = [&](int i) { return l0 + (i + rot < nsteps ? i + rot : i + rot - nsteps); };
 
   XnIn xi;
