@@ -225,7 +225,8 @@ def cpu_baseline(shape, rot, rows, seconds, single_thread=False):
                num_v_heads=shape.num_v_heads, head_v_dim=shape.head_v_dim, conv_width=shape.conv_width,
                ssm_state_dtype=shape.ssm_state_dtype, has_residual=shape.has_residual,
                qkvz_format=shape.qkvz_format, norm_eps=shape.norm_eps,
-               gated_norm_eps=shape.gated_norm_eps, l2norm_eps=shape.l2norm_eps)
+               gated_norm_eps=shape.gated_norm_eps, l2norm_eps=shape.l2norm_eps,
+               mx_scale_rule=shape.mx_scale_rule)
     w = {k: (bits(v) if v.dtype == torch.bfloat16 else v.numpy()) for k, v in rot.w_cpu.tensors().items()}
     c = rot.call_cpu
     x, res = bits(c.x[:rows]), bits(c.residual[:rows])

@@ -20,12 +20,14 @@ GDN_FMT_MXFP4 = 1
 GDN_FMT_MXFP6 = 2
 GDN_STATE_F32 = 0
 GDN_STATE_BF16 = 1
+GDN_MXSCALE_ROUNDED_MAX = 0
+GDN_MXSCALE_CEIL = 1
 GDN_MAX_ROWS = 16
 
 EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error",
             "gdn_block_packed_weight_bytes", "gdn_block_pack_weights", "gdn_block_check",
             "gdn_mxfp4_quantize", "gdn_block_decode_with_out_proj", "gdn_mxfp6_round_weights",
-            "gdn_block_verify")
+            "gdn_block_verify", "gdn_block_set_spin_limit")
 
 
 class GdnBlockConfig(ctypes.Structure):
@@ -35,7 +37,7 @@ class GdnBlockConfig(ctypes.Structure):
         ("num_state_slots", c_int32), ("max_rows", c_int32), ("qkvz_format", c_int32),
         ("ssm_state_dtype", c_int32), ("has_residual", c_int32),
         ("norm_eps", c_float), ("gated_norm_eps", c_float), ("l2norm_eps", c_float),
-        ("input_normed", c_int32), ("fold_out_proj", c_int32),
+        ("input_normed", c_int32), ("fold_out_proj", c_int32), ("mx_scale_rule", c_int32),
     ]
 
 
@@ -81,11 +83,13 @@ def load() -> ctypes.CDLL:
         lib.gdn_block_pack_weights.restype = c_int
         lib.gdn_block_check.argtypes = [c_void_p, POINTER(c_uint32)]
         lib.gdn_block_check.restype = c_int
+        lib.gdn_block_set_spin_limit.argtypes = [c_void_p, c_int32]
+        lib.gdn_block_set_spin_limit.restype = c_int
         lib.gdn_block_decode_with_out_proj.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(GdnBlockWeights),
                                                        c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                                        c_void_p]
         lib.gdn_block_decode_with_out_proj.restype = c_int
-        lib.gdn_mxfp4_quantize.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
+        lib.gdn_mxfp4_quantize.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_int32, c_void_p]
         lib.gdn_mxfp4_quantize.restype = c_int
         lib.gdn_mxfp6_round_weights.argtypes = [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]
         lib.gdn_mxfp6_round_weights.restype = c_int
@@ -152,10 +156,17 @@ def gdn_block_check(handle) -> int:
     return int(word.value)
 
 
-def gdn_mxfp4_quantize(x: int, rows: int, cols: int, codes: int, scales: int, stream: int) -> None:
-    rc = load().gdn_mxfp4_quantize(x, rows, cols, codes, scales, stream)
+def gdn_mxfp4_quantize(x: int, rows: int, cols: int, codes: int, scales: int, scale_rule: int,
+                       stream: int) -> None:
+    rc = load().gdn_mxfp4_quantize(x, rows, cols, codes, scales, scale_rule, stream)
     if rc != GDN_OK:
         raise GdnError(rc, gdn_block_last_error(None))
+
+
+def gdn_block_set_spin_limit(handle, polls: int) -> None:
+    rc = load().gdn_block_set_spin_limit(handle, polls)
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(handle))
 
 
 def gdn_mxfp6_round_weights(w: int, rows: int, cols: int, codes: int, scales: int, stream: int) -> None:

@@ -8,7 +8,7 @@ from __future__ import annotations
 import torch
 
 from . import abi
-from .configs import FMT_MXFP4, FMT_MXFP6, SSM_BF16, GdnShape
+from .configs import FMT_MXFP4, FMT_MXFP6, MX_SCALE_CEIL, SSM_BF16, GdnShape
 
 _FMT = {FMT_MXFP4: abi.GDN_FMT_MXFP4, FMT_MXFP6: abi.GDN_FMT_MXFP6}
 
@@ -23,7 +23,8 @@ def make_config(shape: GdnShape, max_rows: int | None = None) -> abi.GdnBlockCon
         ssm_state_dtype=abi.GDN_STATE_BF16 if s.ssm_state_dtype == SSM_BF16 else abi.GDN_STATE_F32,
         has_residual=1 if s.has_residual else 0,
         norm_eps=s.norm_eps, gated_norm_eps=s.gated_norm_eps, l2norm_eps=s.l2norm_eps,
-        input_normed=1 if s.input_normed else 0, fold_out_proj=1 if s.fold_out_proj else 0)
+        input_normed=1 if s.input_normed else 0, fold_out_proj=1 if s.fold_out_proj else 0,
+        mx_scale_rule=abi.GDN_MXSCALE_CEIL if s.mx_scale_rule == MX_SCALE_CEIL else abi.GDN_MXSCALE_ROUNDED_MAX)
 
 
 def _check(t: torch.Tensor, name: str, dtype, shape, device):
@@ -101,6 +102,10 @@ class GdnBlock:
         _check(packed, "packed", torch.uint8, (abi.gdn_block_packed_weight_bytes(self.handle),), self.device)
         st.w_proj_packed = packed.data_ptr()
         return st
+
+    def set_spin_limit(self, polls: int) -> None:
+        """Poll limit of the bounded waits of later decodes (see the header)."""
+        abi.gdn_block_set_spin_limit(self.handle, polls)
 
     def check(self) -> int:
         """Sticky error word of this handle's decodes (0 = every wait completed)."""

@@ -22,6 +22,10 @@ SSM_BF16 = "bf16"
 FMT_BF16 = "bf16"
 FMT_MXFP4 = "mxfp4"
 FMT_MXFP6 = "mxfp6"
+# scale rules of the MXFP4 activation quantiser: the block maximum rounded at e2m1's
+# mantissa, exponent - 2 (the default); or the smallest power of two with max <= 6 * scale
+MX_SCALE_ROUNDED_MAX = "rounded_max"
+MX_SCALE_CEIL = "ceil"
 
 
 @dataclass(frozen=True)
@@ -42,6 +46,7 @@ class GdnShape:
     l2norm_eps: float = 1e-6
     input_normed: bool = False   # x is already the norm's output (no residual add, no norm)
     fold_out_proj: bool = False  # also write the out_proj partial [R, H] from the core rows
+    mx_scale_rule: str = MX_SCALE_ROUNDED_MAX  # MXFP4 activation scale rule
     # workload fields: the row counts this shape is exercised at, whether pad
     # rows are mixed in, and how many layer copies a timing run rotates over
     rows: tuple = (1,)

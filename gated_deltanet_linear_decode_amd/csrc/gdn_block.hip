@@ -89,7 +89,7 @@ constexpr int kLine = 32;          // uint32 words per 128-byte line: one hot co
 #define GDN_WINDOW 8
 #endif
 constexpr int kWin = GDN_WINDOW;
-constexpr int kSpinLimit = 1 << 20;
+constexpr int kSpinLimit = 1 << 20;  // default poll limit of a bounded wait (Args::spin)
 constexpr int kNormCopies = 8;     // the norm-done counter is kept on 8 lines, polled spread out
 constexpr int kGroupCopies = 8;    // a key-head group's tiles-done counter is spread over 8 lines
 constexpr int kCoreCopies = 16;    // so is the core-done counter of the out_proj fold, on 16
@@ -157,14 +157,14 @@ __device__ __forceinline__ void st_agent16(uint32_t* p, u32x4_t v) {
 
 // The whole workgroup waits until a counter reaches `target`. Wave 0 polls, backing off
 // between polls so that waiting workgroups do not crowd the counter's memory channel;
-// it gives up after kSpinLimit polls, recording `code`. No memory access after the call
+// it gives up after `limit` polls, recording `code`. No memory access after the call
 // is moved above it.
-__device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t target, uint32_t* err, uint32_t code) {
+__device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t target, uint32_t* err, uint32_t code, int limit) {
   if (threadIdx.x < 64) {
     int it = 0;
     while (ld_agent(ctr) < target) {
       __builtin_amdgcn_s_sleep(4);
-      if (++it > kSpinLimit) {
+      if (++it > limit) {
         __hip_atomic_fetch_or(err, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -261,6 +261,9 @@ struct Args {
   int S, Kr, G, Gq;              // K ranges (splits) of Kr each, projection workgroups, of which
                                  // in_proj_qkvz ones
   int nk, dk, nv, dv, r, GW, Cd, slots;
+  int PW;      // floats per row of the split partials: Nq + Nb rounded up to whole 128-byte lines
+  int spin;    // poll limit of every bounded wait
+  int mx_ceil; // MXFP4 activation scale rule: 0 rounded maximum, 1 ceiling
   float eps, l2eps, geps;
 };
 
@@ -276,23 +279,31 @@ __device__ __forceinline__ int sy_conv(const Args& a, int n, int g) {
 constexpr int kNormMaxChunks = 8;  // 16-byte chunks per thread: H <= 8 * 8 * 256
 
 // MXFP4 quantisation of one 32-element block held by 4 consecutive lanes, 8 bf16 each
-// (dwords in element order, the even element in the low half). The block exponent is the
-// smallest e with max|x| <= 6 * 2^e, clamped below at -126; with max|x| = M * 2^E
-// (1 <= M < 2) that is E - 2, plus 1 when M > 1.5. Each x / 2^e (exact: a power-of-two
-// scaling) is rounded to the nearest e2m1 value, ties to the even code: the code counts
-// the rounding boundaries 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 that |x| / 2^e passes (a
-// boundary that is a tie belongs to the even side). A zero code carries no sign.
-// ("vLLM PR #60833", Details / MoE: dynamic MXFP4 in 1x32 blocks with RCEIL scales.)
-// All 4 lanes of the block must be active. Returns the 8 codes (element 8 j + q in nibble
-// q); the scale byte e + 127 goes to `ebyte`.
-__device__ __forceinline__ uint32_t mx_quant8(const uint32_t* v, uint32_t& ebyte) {
+// (dwords in element order, the even element in the low half) ("vLLM PR #60833", Details
+// / MoE: dynamic MXFP4 in 1x32 blocks; Details / MXFP4 layouts: two roundings of the
+// scale). With max|x| = M * 2^E (1 <= M < 2, read off the bf16 bits of the maximum) the
+// block exponent e is E - 2 plus a carry, clamped below at -126 (a zero or subnormal
+// maximum gives -126):
+//   ceil == 0, the rounded maximum (the same page's account of dynamic_mxfp4_quant, in the
+//     reviewer's comment proposing MXFP6): M rounded half up at e2m1's one mantissa bit
+//     carries when M >= 1.75, i.e. when the top two of the 7 mantissa bits are set;
+//   ceil == 1, the smallest e with max|x| <= 6 * 2^e: a carry when M > 1.5.
+// Each x / 2^e (exact: a power-of-two scaling) is rounded to the nearest e2m1 value, ties
+// to the even code: the code counts the rounding boundaries 0.25, 0.75, 1.25, 1.75, 2.5,
+// 3.5, 5 that |x| / 2^e passes (a boundary that is a tie belongs to the even side); a value
+// past 6 (up to 7 with the rounded maximum) takes the top code. A zero code carries no
+// sign. All 4 lanes of the block must be active. Returns the 8 codes (element 8 j + q in
+// nibble q); the scale byte e + 127 goes to `ebyte`.
+__device__ __forceinline__ uint32_t mx_quant8(const uint32_t* v, uint32_t& ebyte, int ceil) {
   uint32_t m = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) m = max(m, max(v[q] & 0x7fffu, (v[q] >> 16) & 0x7fffu));
   m = max(m, (uint32_t)__shfl_xor((int)m, 1, 64));
   m = max(m, (uint32_t)__shfl_xor((int)m, 2, 64));
   const int ef = (int)(m >> 7);
-  const int e = ef == 0 ? -126 : max(-126, ef - 129 + ((m & 0x7fu) > 0x40u ? 1 : 0));
+  const uint32_t mant = m & 0x7fu;
+  const int carry = ceil ? (mant > 0x40u ? 1 : 0) : (mant >= 0x60u ? 1 : 0);
+  const int e = ef == 0 ? -126 : max(-126, ef - 129 + carry);
   const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e
   uint32_t codes = 0;
 #pragma unroll
@@ -373,7 +384,7 @@ __device__ void norm_role(const Args& a, int b, float* red) {
     if (MX) {
       // H is a multiple of 512, so a wave's 64 chunks are all in range together
       uint32_t v[4] = {o4[0], o4[1], o4[2], o4[3]}, eb;
-      st_agent(a.xq + (size_t)row * (H >> 3) + mi, mx_quant8(v, eb));
+      st_agent(a.xq + (size_t)row * (H >> 3) + mi, mx_quant8(v, eb, a.mx_ceil));
       // The wave's 64 chunks are the 16 blocks of 4 K steps of 128: block 4 s + kb holds
       // K quarter kb of step s. Scales are stored per (4 steps, quarter kb) as one dword,
       // byte s, the operand a projection lane of quarter kb reads for 4 steps at once.
@@ -391,7 +402,7 @@ __device__ void norm_role(const Args& a, int b, float* red) {
   // The residual row is rewritten with h, each workgroup its own slice. With a residual
   // input every workgroup of the row reads the whole row first: the rewrite waits until
   // every norm workgroup has counted itself (so has finished loading).
-  if (a.has_res) wait_count(sy(a, kSyNorm + b % kNormCopies), (uint32_t)(a.R * a.P), sy(a, kSyError), kErrNormWait);
+  if (a.has_res) wait_count(sy(a, kSyNorm + b % kNormCopies), (uint32_t)(a.R * a.P), sy(a, kSyError), kErrNormWait, a.spin);
   if (mi < nchunk) rp[mi] = mine;
   wait_stores();
   __syncthreads();
@@ -430,7 +441,7 @@ __device__ __forceinline__ void publish_reduced(const Args& a, int t, int s, f32
   const int src = (em & 3) * 64 + (em >> 2) * 16 + en;
   const float v = ((red[0][src] + red[1][src]) + red[2][src]) + red[3][src];
   const int ch = (isq ? t * 16 : a.Nq + (t - a.Tq) * 16) + em;  // channel in [qkvz | ba] order
-  if (en < a.R && (isq || ch < a.Nq + a.Nb)) st_agent(&a.part[((size_t)s * a.R + en) * (a.Nq + a.Nb) + ch], v);
+  if (en < a.R && (isq || ch < a.Nq + a.Nb)) st_agent(&a.part[((size_t)s * a.R + en) * a.PW + ch], v);
   wait_stores();
   __syncthreads();
   if (tid == 0) add_agent(sy(a, kSyBa), 1u);  // only b|a tiles are published this way
@@ -444,7 +455,7 @@ __device__ __forceinline__ void publish_tiles(const Args& a, int t0, int s, f32x
   if (en < a.R) {  // the lane's 4 channels are adjacent: one 16-byte store
     const int ch = (t0 + wave) * 16 + 4 * (lane >> 4);
     const u32x4_t v = {__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])};
-    st_agent16(reinterpret_cast<uint32_t*>(&a.part[((size_t)s * a.R + en) * (a.Nq + a.Nb) + ch]), v);
+    st_agent16(reinterpret_cast<uint32_t*>(&a.part[((size_t)s * a.R + en) * a.PW + ch]), v);
   }
   wait_stores();
   __syncthreads();
@@ -467,7 +478,7 @@ __device__ __forceinline__ void wait_group(const Args& a, int g) {
     int it = 0;
     while (!__all(share == 0 || ld_agent(ctr) >= (uint32_t)share)) {
       __builtin_amdgcn_s_sleep(4);
-      if (++it > kSpinLimit) {
+      if (++it > a.spin) {
         if (c == 0) __hip_atomic_fetch_or(sy(a, kSyError), kErrGroupWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -503,7 +514,7 @@ __device__ __forceinline__ const u32x4_t* wptr(const Args& a, int t, int s, int 
 
 // waits for the norm rows, then copies xn[0..R)[k0, k0 + Kr) into LDS
 __device__ __forceinline__ void stage_xn(const Args& a, int gb, int k0, ProjShared& sh) {
-  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)(a.R * a.P), sy(a, kSyError), kErrNormWait);
+  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)(a.R * a.P), sy(a, kSyError), kErrNormWait, a.spin);
   TRACE_POINT(1);
   // 16-byte chunks: cpr per row (<= 128), so each pass of the workgroup covers rpp >= 2 rows
   const int cpr = a.Kr >> 3, rpp = kThreads / cpr, r0 = threadIdx.x / cpr, q = threadIdx.x - r0 * cpr;
@@ -578,7 +589,7 @@ __device__ __forceinline__ void xqin_store(const Args& a, const XnIn& in, ProjSh
     if (pr < a.R * nu) {  // uniform over the wave
       const uint32_t v[4] = {in.v[i][0], in.v[i][1], in.v[i][2], in.v[i][3]};
       uint32_t eb;
-      *reinterpret_cast<uint32_t*>(lds + row * kMxRow + 4 * (unit * 64 + lane)) = mx_quant8(v, eb);
+      *reinterpret_cast<uint32_t*>(lds + row * kMxRow + 4 * (unit * 64 + lane)) = mx_quant8(v, eb, a.mx_ceil);
       // block 4 st + kb of the unit is K quarter kb of step st: one dword per quarter, byte st
       uint32_t d = 0;
 #pragma unroll
@@ -686,7 +697,7 @@ __device__ __forceinline__ void mx_wload(const Args& a, int t, int U, int lane, 
 // waits for the norm rows, then copies the MXFP4 image of xn[0..R)[k0, k0 + Kr) into LDS:
 // codes at row * kMxRow, scale dwords (grouped per unit as in the global image) after them
 __device__ __forceinline__ void stage_xq(const Args& a, int gb, int k0, ProjShared& sh) {
-  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)(a.R * a.P), sy(a, kSyError), kErrNormWait);
+  wait_count(sy(a, kSyNorm + gb % kNormCopies), (uint32_t)(a.R * a.P), sy(a, kSyError), kErrNormWait, a.spin);
   TRACE_POINT(1);
   uint8_t* lds = reinterpret_cast<uint8_t*>(&sh.xs[0][0]);
   // 16-byte code chunks: cpr per row (<= 32), rpp >= 8 rows per pass; scale dwords: spr per
@@ -959,12 +970,16 @@ __device__ __forceinline__ void conv_store(const Args& a, int slot, const ConvIn
   st[(size_t)(kConvW - 2) * a.Cd] = f2bf(y);
 }
 
-// The split partials live split-major ([S, R, Nq + Nb]), so a projection workgroup stores
-// them with 16-byte stores. A reader takes 4 adjacent channels of row n per 16-byte load,
-// S loads in one straight sequence (split indices past S repeat the last one, so the
-// compiler issues them back to back), and adds them in split order. Plain loads are safe
-// here: nothing reads a partial before its tiles' counter completes, and caches start
-// each launch clean.
+// The split partials live split-major ([S, R, PW]), so a projection workgroup stores them
+// with 16-byte stores. A reader takes 4 adjacent channels of row n per 16-byte load, S
+// loads in one straight sequence (split indices past S repeat the last one, so the
+// compiler issues them back to back), and adds them in split order. Plain (cached) loads
+// are safe because no 128-byte line holds partials of two hand-offs: a row of PW floats
+// is whole lines, each key-head group's channels are whole lines (a group is a multiple
+// of 64 channels) and so is the b|a block after them (padded to 32 channels). A line is
+// therefore first read only after every workgroup that writes it has been counted, so no
+// cache (a CU's, or an XCD's L2) can hold a copy older than its data; caches start each
+// launch clean.
 constexpr int kMaxSplits = 16;
 template <int N>
 __device__ __forceinline__ f32x4_t sum_splits4(const f32x4_t* base, size_t stride, int S) {
@@ -990,7 +1005,7 @@ __device__ __forceinline__ float sum_splits1(const float* base, size_t stride, i
 }
 // projection outputs (bf16 values) of channels ch .. ch + 3 of row n (ch a multiple of 4)
 __device__ __forceinline__ f32x4_t proj_quad(const Args& a, int n, int ch) {
-  const size_t nn = (size_t)(a.Nq + a.Nb);
+  const size_t nn = (size_t)a.PW;
   const f32x4_t* base = reinterpret_cast<const f32x4_t*>(a.part + (size_t)n * nn + ch);
   const size_t stride = a.R * nn / 4;
   f32x4_t v = a.S <= 4 ? sum_splits4<4>(base, stride, a.S)
@@ -1001,7 +1016,7 @@ __device__ __forceinline__ f32x4_t proj_quad(const Args& a, int n, int ch) {
 }
 // projection output (a bf16 value) of channel ch of row n
 __device__ __forceinline__ float proj_one(const Args& a, int n, int ch) {
-  const size_t nn = (size_t)(a.Nq + a.Nb);
+  const size_t nn = (size_t)a.PW;
   const float* base = a.part + (size_t)n * nn + ch;
   const size_t stride = a.R * nn;
   return rbf(a.S <= 4 ? sum_splits1<4>(base, stride, a.S)
@@ -1070,14 +1085,14 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
 
   // every recurrence workgroup waits, pad rows included (see the counter clearing below)
   wait_group(a, kap);
-  wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.S), sy(a, kSyError), kErrGroupWait);
+  wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.S), sy(a, kSyError), kErrGroupWait, a.spin);
   TRACE_POINT(1);
 
   uint32_t exit_ticket = 0;
   if (valid) {
     const int gbase = kap * a.GW;
     if (qk_owner && a.r > 1)  // the key head's other value heads have read the old q|k conv rows
-      wait_count(sy(a, sy_conv(a, seq, kap)), (uint32_t)(a.r - 1), sy(a, kSyError), kErrConvWait);
+      wait_count(sy(a, sy_conv(a, seq, kap)), (uint32_t)(a.r - 1), sy(a, kSyError), kErrConvWait, a.spin);
     // q | k | v | z channel of quad j (a multiple of 4) in block blk of the head's group
     auto qch = [&](int blk, int j) {
       return gbase + (blk == 0 ? j : blk == 1 ? DK + j : blk == 2 ? 2 * DK + hh * DV + j
@@ -1247,8 +1262,8 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   if (tid == 128 && exit_ticket == (uint32_t)(a.Rs * a.nv - 1)) {
     // the norm workgroups may still be rewriting residual rows (past their last wait)
     int it = 0;
-    while (ld_agent(sy(a, kSyNormExit)) < (uint32_t)(a.R * a.P) && ++it <= kSpinLimit) __builtin_amdgcn_s_sleep(4);
-    if (it > kSpinLimit) __hip_atomic_fetch_or(sy(a, kSyError), kErrNormWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (ld_agent(sy(a, kSyNormExit)) < (uint32_t)(a.R * a.P) && ++it <= a.spin) __builtin_amdgcn_s_sleep(4);
+    if (it > a.spin) __hip_atomic_fetch_or(sy(a, kSyError), kErrNormWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st_agent(sy(a, kSyNormExit), 0u);
     for (int c = 0; c < kNormCopies; ++c) st_agent(sy(a, kSyNorm + c), 0u);
     st_agent(sy(a, kSyBa), 0u);
@@ -1282,7 +1297,8 @@ __device__ void oproj_role(const Args& a, int ob, ProjShared& sh) {
   for (int u = 0; u < kOutSteps; ++u)
     if (u < nsteps) w[u] = __builtin_nontemporal_load(wop(u));
 
-  wait_count(sy(a, kSyCoreDone + ob % kCoreCopies), (uint32_t)(a.Rs * a.nv), sy(a, kSyError), kErrGroupWait);
+  wait_count(sy(a, kSyCoreDone + ob % kCoreCopies), (uint32_t)(a.Rs * a.nv), sy(a, kSyError), kErrGroupWait,
+             a.spin);
   TRACE_POINT(1);
   // core rows [R, K] into LDS with direct-to-LDS loads, all in flight at once (plain
   // loads: first read after the count). One wave instruction fills 1 KiB of LDS, 16 bytes
@@ -1479,14 +1495,14 @@ __global__ __launch_bounds__(kThreads) void mx6_round_kernel(const uint16_t* __r
 // rows of bf16 -> MXFP4 codes [rows, cols/2] (low nibble = even element) and e8m0 scales
 // [rows, cols/32], with the quantiser of the decode kernel; one workgroup per row
 __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __restrict__ x, uint32_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales, int cols) {
+                                                            uint8_t* __restrict__ scales, int cols, int ceil) {
   const int row = blockIdx.x, nchunk = cols >> 3;
   for (int i = threadIdx.x; i < nchunk; i += kThreads) {
     // chunks of one 32-block sit on 4 consecutive lanes, which are active together
     const uint4 q = *reinterpret_cast<const uint4*>(x + (size_t)row * cols + 8 * i);
     const uint32_t v[4] = {q.x, q.y, q.z, q.w};
     uint32_t eb;
-    codes[(size_t)row * nchunk + i] = mx_quant8(v, eb);
+    codes[(size_t)row * nchunk + i] = mx_quant8(v, eb, ceil);
     if ((i & 3) == 0) scales[(size_t)row * (cols >> 5) + (i >> 2)] = (uint8_t)eb;
   }
 }
@@ -1500,6 +1516,8 @@ struct gdn_block {
   gdn_block_config cfg;
   int device;
   int nq, nb, cd, tq, tb, t, splits, steps, sync_words;
+  int pw;             // floats per row of the split partials (whole 128-byte lines)
+  int spin;           // poll limit of the bounded waits
   int kr;             // K range of a projection workgroup
   bool fold;          // out_proj folded in
   int o, ko;          // out_proj workgroups (4 tiles of 16 columns of H each) and K (nv * dv)
@@ -1564,6 +1582,8 @@ std::string check_config(const gdn_block_config* c) {
   if (c->input_normed == 1 && c->has_residual == 1)
     add("input_normed takes the norm's output as x: has_residual must be 0");
   if (c->fold_out_proj != 0 && c->fold_out_proj != 1) add("fold_out_proj must be 0 or 1");
+  if (c->mx_scale_rule != GDN_MXSCALE_ROUNDED_MAX && c->mx_scale_rule != GDN_MXSCALE_CEIL)
+    add("mx_scale_rule must be GDN_MXSCALE_ROUNDED_MAX or GDN_MXSCALE_CEIL");
   if (c->fold_out_proj == 1) {
     const long long kv = (long long)c->num_v_heads * c->head_v_dim;
     if (kv % 128 != 0 || kv > 1024)
@@ -1641,6 +1661,10 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   b->tq = b->nq / 16;
   b->tb = (b->nb + 15) / 16;
   b->t = b->tq + b->tb;
+  // a partial row: the in_proj_qkvz channels (key-head groups of a multiple of 64 channels,
+  // so whole 128-byte lines), then the b|a channels padded to whole lines
+  b->pw = b->nq + (int)align_up((size_t)b->nb, 32);
+  b->spin = kSpinLimit;
   b->steps = H / 32;
   b->fmt = cfg->qkvz_format == GDN_FMT_MXFP4 ? kFmtMx4 : cfg->qkvz_format == GDN_FMT_MXFP6 ? kFmtMx6 : kFmtBf16;
   b->mx = b->fmt == kFmtMx4;
@@ -1665,7 +1689,7 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
     return o;
   };
   const size_t o_xn = take((size_t)R * H * 2);
-  const size_t o_part = take((size_t)S * R * (b->nq + b->nb) * 4);
+  const size_t o_part = take((size_t)S * R * b->pw * 4);
   const size_t o_sync = take((size_t)b->sync_words * 4);
   const size_t o_xq = b->mx ? take((size_t)R * H / 2) : 0;
   const size_t o_xqs = b->mx ? take((size_t)R * H / 32) : 0;
@@ -1861,6 +1885,9 @@ int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_wei
   a.eps = c.norm_eps;
   a.l2eps = c.l2norm_eps;
   a.geps = c.gated_norm_eps;
+  a.PW = b->pw;
+  a.spin = b->spin;
+  a.mx_ceil = c.mx_scale_rule == GDN_MXSCALE_CEIL ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // no norm workgroups with a normed input; the out_proj workgroups last
@@ -1910,10 +1937,22 @@ extern "C" int gdn_block_check(gdn_block_t b, uint32_t* error_word) {
   if (!b || !error_word) return GDN_E_INVALID_ARG;
   uint32_t v = 0;
   uint32_t* word = b->sync + (size_t)kSyError * kLine;
-  hipError_t e = hipMemcpy(&v, word, 4, hipMemcpyDeviceToHost);
-  if (e == hipSuccess && v) e = hipMemset(word, 0, 4);
+  // every enqueued launch has ended, on every stream of the device
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(&v, word, 4, hipMemcpyDeviceToHost);
+  // A launch whose wait gave up may have left hand-off counters uncleared (their
+  // clearing assumes that every workgroup arrived): clear all of them, and the word.
+  if (e == hipSuccess && v) e = hipMemset(b->sync, 0, (size_t)b->sync_words * 4);
+  if (e == hipSuccess && v) e = hipDeviceSynchronize();
   if (e != hipSuccess) return fail(b, GDN_E_HIP, std::string("gdn_block_check: ") + hipGetErrorString(e));
   *error_word = v;
+  return GDN_OK;
+}
+
+extern "C" int gdn_block_set_spin_limit(gdn_block_t b, int32_t polls) {
+  if (!b) return GDN_E_INVALID_ARG;
+  if (polls < 0) return fail(b, GDN_E_INVALID_ARG, "gdn_block_set_spin_limit: polls must be >= 0");
+  b->spin = polls;
   return GDN_OK;
 }
 
@@ -1927,7 +1966,11 @@ extern "C" int gdn_block_trace_copy(unsigned long long* host, size_t blocks) {
 #endif
 
 extern "C" int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, void* codes, void* scales,
-                                  void* stream) {
+                                  int32_t scale_rule, void* stream) {
+  if (scale_rule != GDN_MXSCALE_ROUNDED_MAX && scale_rule != GDN_MXSCALE_CEIL) {
+    g_create_error = "gdn_mxfp4_quantize: scale_rule must be GDN_MXSCALE_ROUNDED_MAX or GDN_MXSCALE_CEIL";
+    return GDN_E_INVALID_ARG;
+  }
   if (rows < 0 || cols <= 0 || cols % 32 != 0) {
     g_create_error = "gdn_mxfp4_quantize: rows must be >= 0 and cols a positive multiple of 32 (got rows " +
                      std::to_string(rows) + ", cols " + std::to_string(cols) + ")";
@@ -1944,7 +1987,7 @@ extern "C" int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, voi
   if (rows == 0) return GDN_OK;
   hipLaunchKernelGGL(mx_quant_kernel, dim3(rows), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint16_t*>(x), static_cast<uint32_t*>(codes), static_cast<uint8_t*>(scales),
-                     (int)cols);
+                     (int)cols, scale_rule == GDN_MXSCALE_CEIL ? 1 : 0);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     g_create_error = std::string("gdn_mxfp4_quantize: launch failed: ") + hipGetErrorString(e);

@@ -22,7 +22,7 @@
  *   6. RMSNormGated over each head, norm before gate:
  *      core = bf16(bf16(o) * rstd * gated_norm_w * SiLU(z)).
  *
- * A row whose state index is <= 0 is a pad row: its core row is written as
+ * A row whose state index is <= 0 (or >= num_state_slots) is a pad row: its core row is written as
  * +0.0, and neither conv nor SSM state is touched; its residual row is still
  * written ("sgl-amd-mono PR #89", Modifications; "SGLang PR #43558", Accuracy:
  * pad rows at slot -1).
@@ -66,11 +66,19 @@
  * size of the matrices it copies.
  *
  * MXFP4 activations: with MXFP4 in_proj_qkvz each xn row is quantised inside the
- * decode, per 32-element block: the scale exponent e is the smallest integer with
- * max|xn| <= 6 * 2^e (at least -126), each xn / 2^e is rounded to the nearest e2m1
- * value with ties to the even code, and a zero code carries no sign ("vLLM PR #60833",
- * Details / MoE: dynamic MXFP4, 1x32 blocks, RCEIL scales). gdn_mxfp4_quantize applies
- * the same quantiser to caller rows.
+ * decode, per 32-element block ("vLLM PR #60833", Details / MoE: dynamic MXFP4 in 1x32
+ * blocks; Details / MXFP4 layouts: the GDN projections quantise their inputs with one of
+ * two scale roundings, matching the FP4 GEMM in use). With the block maximum
+ * max|xn| = M * 2^E (1 <= M < 2) the scale is 2^e, e clamped to [-126, 127] (an all-zero
+ * block keeps 2^-126), by the config's mx_scale_rule:
+ *   GDN_MXSCALE_ROUNDED_MAX (default): the maximum rounded half up at e2m1's one mantissa
+ *     bit, e = its exponent - 2, i.e. e = E - 2, or E - 1 when M >= 1.75 (the rule the
+ *     same page's reviewer comment proposing MXFP6 gives for dynamic_mxfp4_quant, step 2
+ *     of making the weights); elements up to 7 * 2^e occur and round to 6 * 2^e;
+ *   GDN_MXSCALE_CEIL: the smallest e with max|xn| <= 6 * 2^e, i.e. E - 2, or E - 1 when
+ *     M > 1.5.
+ * Each xn / 2^e is rounded to the nearest e2m1 value with ties to the even code, and a
+ * zero code carries no sign. gdn_mxfp4_quantize applies the same quantiser to caller rows.
  *
  * Errors: every function returns GDN_OK (0) or a negative code; the message
  * is kept per handle (gdn_block_last_error). A failed check enqueues nothing.
@@ -97,6 +105,9 @@ extern "C" {
 
 #define GDN_STATE_F32 0
 #define GDN_STATE_BF16 1
+
+#define GDN_MXSCALE_ROUNDED_MAX 0 /* MXFP4 activation scale: rounded block maximum, exponent - 2 */
+#define GDN_MXSCALE_CEIL 1        /* MXFP4 activation scale: smallest 2^e with max <= 6 * 2^e */
 
 #define GDN_MAX_ROWS 16
 
@@ -125,6 +136,9 @@ typedef struct gdn_block_config {
                               Modifications: K1 with out_proj folded in); needs nv*dv a
                               multiple of 128 up to 1024; decode with
                               gdn_block_decode_with_out_proj */
+  int32_t mx_scale_rule;   /* GDN_MXSCALE_ROUNDED_MAX (0) or GDN_MXSCALE_CEIL (1): the scale
+                              rule of the MXFP4 activation quantiser (see above); read only
+                              with qkvz_format GDN_FMT_MXFP4 */
 } gdn_block_config;
 
 typedef struct gdn_block_weights {
@@ -208,12 +222,14 @@ size_t gdn_block_packed_weight_bytes(gdn_block_t blk);
 int gdn_block_pack_weights(gdn_block_t blk, const gdn_block_weights* w, void* packed, void* stream);
 
 /* Quantise `rows` rows of `cols` bf16 values (x, [rows, cols], device, 16-byte aligned)
- * to OCP MXFP4 with the decode's activation quantiser (see above): codes [rows, cols/2]
- * uint8, two per byte, low nibble = even element (device, 4-byte aligned), and scales
- * [rows, cols/32] uint8 e8m0 = e + 127 (device). cols must be a positive multiple of 32;
- * rows == 0 enqueues nothing. Asynchronous on `stream`; allocates nothing. Errors are
- * reported like a failed gdn_block_create (gdn_block_last_error(NULL)). */
-int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, void* codes, void* scales, void* stream);
+ * to OCP MXFP4 with the decode's activation quantiser (see above) under `scale_rule`
+ * (GDN_MXSCALE_ROUNDED_MAX or GDN_MXSCALE_CEIL): codes [rows, cols/2] uint8, two per
+ * byte, low nibble = even element (device, 4-byte aligned), and scales [rows, cols/32]
+ * uint8 e8m0 = e + 127 (device). cols must be a positive multiple of 32; rows == 0
+ * enqueues nothing. Asynchronous on `stream`; allocates nothing. Errors are reported
+ * like a failed gdn_block_create (gdn_block_last_error(NULL)). */
+int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, void* codes, void* scales, int32_t scale_rule,
+                       void* stream);
 
 /* Round `rows` rows of `cols` bf16 weights (w, [rows, cols], device, 16-byte aligned)
  * to MXFP6 E2M3, one block of 32 along a row at a time, and write them in the layout
@@ -228,13 +244,25 @@ int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, void* codes, v
  * allocates nothing. Errors are reported like gdn_mxfp4_quantize's. */
 int gdn_mxfp6_round_weights(const void* w, int32_t rows, int32_t cols, void* codes, void* scales, void* stream);
 
-/* Read and clear the handle's sticky error word (synchronous; not for the hot
- * path). Inside a decode, every wait for another workgroup is bounded; a wait
- * that gives up sets a bit (1: waiting for the norm rows, 2: waiting for a
- * key-head group's projection tiles or, with fold_out_proj, for the core rows, 4:
- * waiting for the other value heads of a key head to read its old q|k conv rows) and
- * lets the launch finish with undefined outputs. 0 means every decode since the last check completed normally. */
+/* Read and clear the handle's sticky error word (synchronous: waits for the whole
+ * device first; not for the hot path). Inside a decode, every wait for another
+ * workgroup is bounded (gdn_block_set_spin_limit); a wait that gives up sets a bit
+ * (1: waiting for the norm rows, 2: waiting for a key-head group's projection tiles or,
+ * with fold_out_proj, for the core rows, 4: waiting for the other value heads of a key
+ * head to read its old q|k conv rows) and lets the launch finish with undefined outputs.
+ * Such a launch can also leave the hand-off counters in the handle's scratch uncleared
+ * (each launch clears them on the assumption that every workgroup arrived), which would
+ * corrupt the handle's next decodes: when the word is not 0, this call also clears every
+ * counter, so decodes enqueued after it start clean. 0 means every decode since the
+ * last check completed normally. */
 int gdn_block_check(gdn_block_t blk, uint32_t* error_word);
+
+/* Set the poll limit of every bounded wait in this handle's later decodes (default
+ * 2^20 polls, each followed by a short sleep: far longer than any launch waits). A
+ * smaller limit makes a stalled launch give up sooner; 0 gives up at the first poll
+ * that does not find the wait complete (used to test the give-up path). polls < 0 is
+ * GDN_E_INVALID_ARG. */
+int gdn_block_set_spin_limit(gdn_block_t blk, int32_t polls);
 
 /* Free the handle and its scratch (NULL is a no-op). Waits for nothing: the
  * caller must make sure no enqueued decode still uses it. */

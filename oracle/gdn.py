@@ -15,9 +15,10 @@ Details / Launches):
   3. y = bf16(W xn) for in_proj_qkvz and in_proj_ba (exact sum, one rounding:
      "SGLang PR #43558", Accuracy, stock GEMM == bf16(fp32(exact sum))).
      MXFP4 in_proj_qkvz: xn is quantised per 32-element block first
-     ("vLLM PR #60833", Details / MoE: dynamic MXFP4, 1x32 blocks, RCEIL).
+     ("vLLM PR #60833", Details / MoE: dynamic MXFP4, 1x32 blocks; Details /
+     MXFP4 layouts: two scale roundings), with either scale rule.
   4. split y into q, k, v, z, b, a (grouped per key head).
-  5. pad row (state index <= 0): core row = +0, no state written.
+  5. pad row (state index <= 0, or past the pool): core row = +0, no state written.
   6. depthwise causal conv update, width 4, no bias, SiLU; the conv state
      keeps the last W-1 raw inputs.
   7. g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b).
@@ -149,15 +150,52 @@ def project_bf16(w_bits, xn_bits):
 E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
-def mxfp4_quantize(v):
+MX_SCALE_ROUNDED_MAX = "rounded_max"
+MX_SCALE_CEIL = "ceil"
+
+
+def mx_block_exponent(amax, mant_bits: int, rule: str = MX_SCALE_ROUNDED_MAX):
+    """Block scale exponent e (scale 2^e) of an MX block with maximum magnitude amax.
+
+    rounded_max: the rule "vLLM PR #60833" (a reviewer's comment proposing MXFP6, how
+    to make the weights, step 2) gives for AITER's dynamic_mxfp4_quant: the block
+    maximum is rounded at the element format's mantissa width (half up, a carry moving
+    into the exponent) and the scale is 2 to the exponent of that rounded maximum minus
+    2. With amax = M 2^E (1 <= M < 2) and m mantissa bits, M rounds up to 2 exactly when
+    floor(M 2^m + 1/2) = 2^(m+1).
+    ceil: the smallest e with amax <= 6 2^e (E2M1's largest magnitude is 6), the literal
+    round-up of amax / 6 to a power of two ("RCEIL"); no element saturates.
+    Both clamp e to [-126, 127]; an all-zero block keeps 2^-126, a normal scale (the
+    all-zero handling of the same page's rounding of step 2, so no 0 / 0).
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    nz = amax > 0
+    safe = np.where(nz, amax, 1.0)
+    if rule == MX_SCALE_ROUNDED_MAX:
+        mant, ex = np.frexp(safe)                      # safe = mant 2^ex, mant in [0.5, 1)
+        M, E = 2.0 * mant, (ex - 1).astype(np.int64)   # safe = M 2^E, M in [1, 2)
+        carry = np.floor(M * 2.0 ** mant_bits + 0.5) >= 2.0 ** (mant_bits + 1)
+        e = E + carry.astype(np.int64) - 2
+    elif rule == MX_SCALE_CEIL:
+        _, p = np.frexp(safe / 6.0)                    # a first guess, adjusted exactly below
+        e = p.astype(np.int64)
+        for _ in range(3):                             # exact comparisons against 6 * 2^e
+            e = np.where(safe > 6.0 * np.exp2(e.astype(np.float64)), e + 1, e)
+            e = np.where(safe <= 6.0 * np.exp2((e - 1).astype(np.float64)), e - 1, e)
+    else:
+        raise ValueError(f"unknown MX scale rule {rule!r}")
+    return np.clip(np.where(nz, e, -126), -126, 127)
+
+
+def mxfp4_quantize(v, rule: str = MX_SCALE_ROUNDED_MAX):
     """Quantise values to OCP MXFP4: e2m1 codes with one e8m0 scale per 32.
 
-    "vLLM PR #60833", Details / MoE: dynamic MXFP4 with 1x32 blocks and RCEIL
-    scales. RCEIL read as: the block exponent e is the smallest integer with
-    max|v| <= 6 * 2^e (so no element saturates), clamped to [-126, 127]; an
-    all-zero block gets e = -126 (a normal scale, never NaN). Each v / 2^e is
-    rounded to the nearest e2m1 value {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to
-    the even code, saturating at 6.
+    "vLLM PR #60833", Details / MoE: dynamic MXFP4 with 1x32 blocks; the same page
+    (Details / MXFP4 layouts) names two roundings of the scale, one per FP4 GEMM
+    family. `rule` picks the block exponent e (mx_block_exponent, with E2M1's one
+    mantissa bit). Each v / 2^e is rounded to the nearest e2m1 value
+    {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even code; values past 6 (the
+    rounded-max rule allows up to 7) take 6, the nearest.
 
     Returns (codes uint8 [..., K], 4-bit sign|magnitude; scale bytes uint8
     [..., K/32] = e + 127).
@@ -165,16 +203,7 @@ def mxfp4_quantize(v):
     v = np.asarray(v, dtype=np.float64)
     blocks = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
     amax = np.abs(blocks).max(axis=-1)
-    e = np.full(amax.shape, -126, dtype=np.int64)
-    nz = amax > 0
-    _, p = np.frexp(amax / 6.0)                  # a first guess, adjusted exactly below
-    e = np.where(nz, p.astype(np.int64), e)
-    for _ in range(3):                           # exact comparisons against 6 * 2^e
-        too_small = nz & (amax > 6.0 * np.exp2(e.astype(np.float64)))
-        e = np.where(too_small, e + 1, e)
-        too_big = nz & (amax <= 6.0 * np.exp2((e - 1).astype(np.float64)))
-        e = np.where(too_big, e - 1, e)
-    e = np.clip(e, -126, 127)
+    e = mx_block_exponent(amax, 1, rule)
     scaled = np.abs(blocks) / np.exp2(e.astype(np.float64))[..., None]
     # nearest e2m1 magnitude, ties to the even code
     d = np.abs(scaled[..., None] - E2M1_VALUES)
@@ -184,7 +213,6 @@ def mxfp4_quantize(v):
     dn = np.take_along_axis(d, nxt[..., None], axis=-1)[..., 0]
     tie = (nxt != best) & (dn == dmin)
     best = np.where(tie & (best % 2 == 1), nxt, best)
-    best = np.where(scaled > 6.0, 7, best)
     sign = (blocks < 0) & (best > 0)
     codes = (best | (sign.astype(np.int64) << 3)).astype(np.uint8)
     return codes.reshape(v.shape), (e + 127).astype(np.uint8)
@@ -208,14 +236,15 @@ def unpack_e2m1(packed):
     return out
 
 
-def project_mxfp4(w_packed, w_scales, xn_bits):
+def project_mxfp4(w_packed, w_scales, xn_bits, rule: str = MX_SCALE_ROUNDED_MAX):
     """y = bf16(sum over K of dequant(W) * dequant(quant(xn))) for MXFP4 weights.
 
     The activation xn (bf16) is quantised per row and 32-block by
-    mxfp4_quantize; both operands' products are exact and summed in float64.
+    mxfp4_quantize with the scale rule `rule`; both operands' products are exact
+    and summed in float64.
     """
     w = mxfp4_dequantize(unpack_e2m1(w_packed), w_scales)
-    xq_codes, xq_scales = mxfp4_quantize(bf16_to_f64(xn_bits))
+    xq_codes, xq_scales = mxfp4_quantize(bf16_to_f64(xn_bits), rule)
     xq = mxfp4_dequantize(xq_codes, xq_scales)
     return f64_to_bf16(xq @ w.T)
 
@@ -235,23 +264,21 @@ E2M3_VALUES = np.array([m / 8.0 for m in range(8)] +
 def mxfp6_round(v):
     """The pages' rounding of weights onto MXFP6 E2M3, one block of 32 along K at a time.
 
-    The block scale follows the MXFP4 RCEIL scheme with the E2M3 maximum 7.5: the block
-    maximum is rounded to 3 mantissa bits (half up, a carry moving into the exponent), and
-    with E the exponent of that rounded maximum the scale is 2^(E - 2), clamped to
-    2^[-126, 127] (an all-zero block keeps 2^-126, a normal scale). Each |v| / scale is
-    rounded to the nearest E2M3 magnitude, ties to the even code (steps of 1/8 below 2,
-    1/4 below 4, 1/2 above), saturating at 7.5. A zero code carries no sign.
+    The block scale is the rounded-maximum rule of mx_block_exponent with E2M3's 3
+    mantissa bits (the same page names it as AITER's dynamic_mxfp4_quant with the E2M3
+    maximum of 7.5): the block maximum is rounded to 3 mantissa bits (half up, a carry
+    moving into the exponent), and with E the exponent of that rounded maximum the scale
+    is 2^(E - 2), clamped to 2^[-126, 127] (an all-zero block keeps 2^-126, a normal
+    scale). Each |v| / scale is rounded to the nearest E2M3 magnitude, ties to the even
+    code (steps of 1/8 below 2, 1/4 below 4, 1/2 above), saturating at 7.5. A zero code
+    carries no sign.
 
     Returns (codes uint8 [..., K] with the sign at bit 5, scale bytes uint8 [..., K/32]).
     """
     v = np.asarray(v, dtype=np.float64)
     blocks = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
     amax = np.abs(blocks).max(axis=-1)
-    mant, ex = np.frexp(amax)                    # amax = mant * 2^ex, mant in [0.5, 1)
-    E = (ex - 1).astype(np.int64)                # amax = (2 mant) 2^E, 2 mant in [1, 2)
-    E = E + (2.0 * mant >= 1.9375)               # 1.111 1b and above round up to 2
-    e = np.where(amax > 0, E - 2, -126)
-    e = np.clip(e, -126, 127)
+    e = mx_block_exponent(amax, 3, MX_SCALE_ROUNDED_MAX)
     a = np.abs(blocks) / np.exp2(e.astype(np.float64))[..., None]
     step = np.where(a < 2.0, 0.125, np.where(a < 4.0, 0.25, 0.5))
     q = np.minimum(np.round(a / step) * step, 7.5)       # np.round: half to even
@@ -416,7 +443,9 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
 
     cfg: hidden, num_k_heads, head_k_dim, num_v_heads, head_v_dim, conv_width,
          ssm_state_dtype ('f32'|'bf16'), has_residual, qkvz_format
-         ('bf16'|'mxfp4'|'mxfp6'), norm_eps, gated_norm_eps, l2norm_eps, and optionally
+         ('bf16'|'mxfp4'|'mxfp6'), norm_eps, gated_norm_eps, l2norm_eps, optionally
+         mx_scale_rule (the MXFP4 activation scale rule, 'rounded_max' unless given;
+         see mx_block_exponent), and optionally
          input_normed: x is already the norm's output xn ("SGLang PR #43558",
          Modifications: the "normed" K1 build starts from input_layernorm's
          output), so the residual add and the norm are skipped and the
@@ -424,7 +453,8 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
     weights: norm_w, w_qkvz (bf16 bits [Nqkvz, H], packed e2m1 [Nqkvz, H/2] or packed
          E2M3 [Nqkvz, H/32, 24]), w_qkvz_scales (MXFP4 and MXFP6 only), w_ba, conv_w, A_log (f32), dt_bias, gated_norm_w.
     x, residual: [R, H] bf16 bits; conv_state [slots, W-1, Cd] bf16 bits;
-    ssm_state [slots, nv, dk, dv] f32 or bf16 bits; state_idx [R] int32.
+    ssm_state [slots, nv, dk, dv] f32 or bf16 bits; state_idx [R] int32. A row whose
+    index is <= 0 or >= slots is a pad row (an index past the pool names no slot).
 
     With weights["w_out"] ([H, nv*dv] bf16 bits) the rank's out_proj partial is
     returned too (out [R, H] bf16 bits; else None).
@@ -444,7 +474,8 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
         h = residual_add(x, residual, cfg["has_residual"])
         xn = gemma_rmsnorm(h, weights["norm_w"], cfg["norm_eps"])
     if cfg["qkvz_format"] == "mxfp4":
-        y_qkvz = project_mxfp4(weights["w_qkvz"], weights["w_qkvz_scales"], xn)
+        y_qkvz = project_mxfp4(weights["w_qkvz"], weights["w_qkvz_scales"], xn,
+                               cfg.get("mx_scale_rule", MX_SCALE_ROUNDED_MAX))
     elif cfg["qkvz_format"] == "mxfp6":
         y_qkvz = project_mxfp6(weights["w_qkvz"], weights["w_qkvz_scales"], xn)
     else:
@@ -457,9 +488,10 @@ def decode_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
     A_log = np.asarray(weights["A_log"], np.float64)
     dt_bias = bf16_to_f64(weights["dt_bias"])
 
+    slots = conv_state.shape[0]
     for row in range(R):
         slot = int(state_idx[row])
-        if slot <= 0:                   # pad row: zero core, no state touched
+        if slot <= 0 or slot >= slots:  # pad row: zero core, no state touched
             continue
         q, k, v, z = split_qkvz(y_qkvz[row], nk, dk, nv, dv)
         b, a = split_ba(y_ba[row], nk, nv)
@@ -518,7 +550,8 @@ def verify_block(cfg: dict, weights: dict, x, residual, conv_state, ssm_state, s
         h = residual_add(x, residual, cfg["has_residual"])
         xn = gemma_rmsnorm(h, weights["norm_w"], cfg["norm_eps"])
     if cfg["qkvz_format"] == "mxfp4":
-        y_qkvz = project_mxfp4(weights["w_qkvz"], weights["w_qkvz_scales"], xn)
+        y_qkvz = project_mxfp4(weights["w_qkvz"], weights["w_qkvz_scales"], xn,
+                               cfg.get("mx_scale_rule", MX_SCALE_ROUNDED_MAX))
     elif cfg["qkvz_format"] == "mxfp6":
         y_qkvz = project_mxfp6(weights["w_qkvz"], weights["w_qkvz_scales"], xn)
     else:

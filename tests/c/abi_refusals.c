@@ -37,8 +37,12 @@ int main(void) {
             strstr(msg, "max_rows"),
         "every reason is listed");
   CHECK(gdn_block_create(NULL, &blk) == GDN_E_INVALID_ARG, "a NULL config is refused");
-  CHECK(gdn_mxfp4_quantize((const void*)0x100000, 1, 48, (void*)0x100000, (void*)0x100000, NULL) ==
-            GDN_E_INVALID_ARG, "cols must be a multiple of 32");
+  CHECK(gdn_mxfp4_quantize((const void*)0x100000, 1, 48, (void*)0x100000, (void*)0x100000, GDN_MXSCALE_ROUNDED_MAX,
+                           NULL) == GDN_E_INVALID_ARG,
+        "cols must be a multiple of 32");
+  CHECK(gdn_mxfp4_quantize((const void*)0x100000, 1, 32, (void*)0x100000, (void*)0x100000, 7, NULL) ==
+            GDN_E_INVALID_ARG, "an unknown scale rule is refused");
+  CHECK(gdn_block_set_spin_limit(NULL, 1) == GDN_E_INVALID_ARG, "a spin limit needs a handle");
   CHECK(gdn_mxfp6_round_weights(NULL, 1, 32, (void*)0x100000, (void*)0x100000, NULL) == GDN_E_INVALID_ARG,
         "NULL weights are refused");
   CHECK(gdn_block_decode(NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, NULL, NULL) == GDN_E_INVALID_ARG,

@@ -19,7 +19,8 @@ def oracle_cfg(shape) -> dict:
                 conv_width=shape.conv_width, ssm_state_dtype=shape.ssm_state_dtype,
                 has_residual=shape.has_residual, qkvz_format=shape.qkvz_format,
                 norm_eps=shape.norm_eps, gated_norm_eps=shape.gated_norm_eps,
-                l2norm_eps=shape.l2norm_eps, input_normed=shape.input_normed)
+                l2norm_eps=shape.l2norm_eps, input_normed=shape.input_normed,
+                mx_scale_rule=shape.mx_scale_rule)
 
 
 def oracle_weights(w) -> dict:

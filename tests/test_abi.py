@@ -61,6 +61,7 @@ def _cfg(**kw):
     ("ssm_state_dtype", 2, "ssm_state_dtype"),
     ("has_residual", 2, "has_residual"),
     ("norm_eps", 0.0, "eps"),
+    ("mx_scale_rule", 2, "mx_scale_rule"),
 ])
 def test_create_refuses_each_bad_field(field, value, needle):
     with pytest.raises(abi.GdnError) as e:
@@ -128,9 +129,12 @@ def test_quantize_arguments_are_checked_on_the_host():
         (1, 32, fake + 8, fake, fake, "aligned"),
         (1, 32, fake, fake + 2, fake, "aligned"),
     ]:
-        assert lib.gdn_mxfp4_quantize(x, rows, cols, codes, scales, None) == abi.GDN_E_INVALID_ARG
+        assert lib.gdn_mxfp4_quantize(x, rows, cols, codes, scales, 0, None) == abi.GDN_E_INVALID_ARG
         assert needle in abi.gdn_block_last_error(None)
-    assert lib.gdn_mxfp4_quantize(fake, 0, 32, fake, fake, None) == abi.GDN_OK  # nothing to do
+    assert lib.gdn_mxfp4_quantize(fake, 1, 32, fake, fake, 2, None) == abi.GDN_E_INVALID_ARG
+    assert "scale_rule" in abi.gdn_block_last_error(None)
+    for rule in (abi.GDN_MXSCALE_ROUNDED_MAX, abi.GDN_MXSCALE_CEIL):
+        assert lib.gdn_mxfp4_quantize(fake, 0, 32, fake, fake, rule, None) == abi.GDN_OK  # nothing to do
 
 
 def test_null_arguments_are_rejected_on_the_host():
@@ -138,4 +142,5 @@ def test_null_arguments_are_rejected_on_the_host():
     assert lib.gdn_block_create(None, None) == abi.GDN_E_INVALID_ARG
     assert "NULL" in abi.gdn_block_last_error(None)
     assert lib.gdn_block_decode(None, None, None, None, None, None, None, 1, None, None) == abi.GDN_E_INVALID_ARG
+    assert lib.gdn_block_set_spin_limit(None, 5) == abi.GDN_E_INVALID_ARG
     lib.gdn_block_destroy(None)  # a no-op

@@ -45,3 +45,21 @@ def test_verify_bytes():
     v = configs.algorithmic_bytes_verify(s, 2, 4)
     assert v == configs.algorithmic_bytes(s, 8, 0) + 2 * slot + 8 * slot
     assert configs.algorithmic_bytes_verify(s, 3, 1) == configs.algorithmic_bytes(s, 3, 3)
+
+
+def test_partial_rows_keep_every_hand_off_on_lines_of_its_own():
+    """The split partials' layout (the decode kernel's [S, R, PW] f32 scratch): for every
+    head shape the library accepts, each key-head group's channels and the b|a block start
+    on a 128-byte line and a row is whole lines, so no line holds partials of two
+    hand-offs (two groups, a group and the b|a block, or two rows)."""
+    for dk in (32, 64, 128):
+        for nk in (1, 2, 3, 4, 8, 16):
+            for r in range(1, 17):
+                nv = nk * r
+                gw = 2 * dk + 2 * r * dk                 # channels of one key-head group
+                nq, nb = nk * gw, 2 * nv
+                pw = nq + -(-nb // 32) * 32              # b|a padded to whole lines
+                assert (gw * 4) % 128 == 0, (dk, nk, r)
+                assert (nq * 4) % 128 == 0 and (pw * 4) % 128 == 0 and pw % 4 == 0, (dk, nk, r)
+                starts = [g * gw for g in range(nk)] + [nq]
+                assert all((4 * c) % 128 == 0 for c in starts)

@@ -1,5 +1,6 @@
 """GPU parity of the MXFP4 in_proj_qkvz path ("vLLM PR #60833", Details / MoE and MXFP4
-layouts: MXFP4 weights with dynamic MXFP4 activations in 1x32 blocks, RCEIL scales).
+layouts: MXFP4 weights with dynamic MXFP4 activations in 1x32 blocks, under either of the
+two scale rules: the rounded block maximum, the default, and the ceiling).
 
 Three kinds of checks:
 
@@ -50,7 +51,8 @@ def _quantizer_inputs(cols, seed):
     t[:, 0] = 6.0
     e = rng.integers(-120, 120, nb).astype(np.float64)
     rows.append(og.f64_to_bf16((t * np.exp2(e)[:, None]).reshape(-1)))
-    # zero blocks, negative zeros, maxima at and just above 1.5 * 2^E
+    # zero blocks, negative zeros, maxima at and just above 1.5 * 2^E (the ceiling's carry)
+    # and at and just below 1.75 * 2^E (the rounded maximum's)
     z = rng.normal(0, 1, (nb, 32))
     z[0::4] = 0.0
     z[1::4] = -0.0
@@ -59,6 +61,11 @@ def _quantizer_inputs(cols, seed):
     zb = og.f64_to_bf16(z.reshape(-1)).reshape(nb, 32)
     zb[3::4, 0] = og.f64_to_bf16(np.array([1.5 * 2.0 ** 3]))[0] + 1  # 1.5 * 2^3 plus one ulp
     rows.append(zb.reshape(-1))
+    m = og.f64_to_bf16(rng.normal(0, 1, (nb, 32)) * 0.2).reshape(nb, 32)
+    top = og.f64_to_bf16(1.75 * np.exp2(rng.integers(-30, 30, nb).astype(np.float64)))
+    m[:, 0] = (top.astype(np.int32) + rng.integers(-1, 1, nb)).astype(np.uint16)  # 1.75 * 2^E, or one ulp below
+    m[:, 1] = og.f64_to_bf16(og.bf16_to_f64(m[:, 0]) * rng.choice([-0.5, 0.25, -0.75], nb))
+    rows.append(m.reshape(-1))
     # subnormal and tiny normal values: the scale exponent clamps at -126
     sub = rng.integers(1, 128, cols).astype(np.uint16) | (rng.integers(0, 2, cols).astype(np.uint16) << 15)
     tiny = og.f64_to_bf16(rng.normal(0, 1, cols) * 2.0 ** -125)
@@ -76,20 +83,22 @@ def _quantizer_inputs(cols, seed):
     return np.stack(rows).astype(np.uint16)
 
 
+@pytest.mark.parametrize("rule", ["rounded_max", "ceil"])
 @pytest.mark.parametrize("cols", [32, 1120, 8192])
-def test_quantizer_bit_exact(cols):
-    """Codes and scales equal the oracle's for every element ("vLLM PR #60833", Details:
-    RCEIL scales; ties to the even code)."""
+def test_quantizer_bit_exact(cols, rule):
+    """Codes and scales equal the oracle's for every element under each scale rule ("vLLM
+    PR #60833", Details: two scale roundings; ties to the even code)."""
     x = _quantizer_inputs(cols, 40 + cols)
     R = x.shape[0]
-    note(f"quantiser rows={R} cols={cols}")
+    note(f"quantiser rows={R} cols={cols} rule={rule}")
     xd = from_u16(x).to(DEV)
     codes = torch.zeros(R, cols // 2, dtype=torch.uint8, device=DEV)
     scales = torch.zeros(R, cols // 32, dtype=torch.uint8, device=DEV)
     abi.gdn_mxfp4_quantize(xd.data_ptr(), R, cols, codes.data_ptr(), scales.data_ptr(),
+                           abi.GDN_MXSCALE_CEIL if rule == "ceil" else abi.GDN_MXSCALE_ROUNDED_MAX,
                            torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    ref_codes, ref_scales = og.mxfp4_quantize(og.bf16_to_f64(x))
+    ref_codes, ref_scales = og.mxfp4_quantize(og.bf16_to_f64(x), rule)
     packed = (ref_codes[:, 0::2] | (ref_codes[:, 1::2] << 4)).astype(np.uint8)
     got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
     assert np.array_equal(got_s, ref_scales), np.argwhere(got_s != ref_scales)[:5]
@@ -101,6 +110,11 @@ def test_quantizer_bit_exact(cols):
 @pytest.mark.parametrize("state", ["f32", "bf16"])
 def test_tiny_mxfp4(rows, state):
     parity_case(TINY_MX.with_(ssm_state_dtype=state), rows, 200 + rows, flips=FLIPS, dev=DEV)
+
+
+@pytest.mark.parametrize("rows", [1, 9, 16])
+def test_tiny_mxfp4_ceil_rule(rows):
+    parity_case(TINY_MX.with_(name="tiny_mxfp4_ceil", mx_scale_rule="ceil"), rows, 210 + rows, flips=FLIPS, dev=DEV)
 
 
 @pytest.mark.parametrize("hidden,dk", [(1536, 32), (2048, 128), (4096, 64)])
@@ -115,6 +129,17 @@ def test_mxfp4_shapes(hidden, dk):
 @pytest.mark.parametrize("rows", [1, 5, 8, 13, 16])
 def test_tp8_rank_mxfp4(rows):
     parity_case(configs.TP8_RANK_MXFP4, rows, 31, flips=FLIPS, dev=DEV)
+
+
+@pytest.mark.parametrize("rows", [1, 8, 16])
+def test_tp8_rank_mxfp4_ceil_rule(rows):
+    parity_case(configs.TP8_RANK_MXFP4.with_(name="tp8_rank_mxfp4_ceil", mx_scale_rule="ceil"), rows, 33,
+                flips=FLIPS, dev=DEV)
+
+
+@pytest.mark.parametrize("rows", [4, 16])
+def test_tp8_rank_mxfp4_gated_norm_weight_near_one(rows):
+    parity_case(configs.TP8_RANK_MXFP4, rows, 34, stress=True, flips=FLIPS, dev=DEV)
 
 
 def test_tp8_rank_mxfp4_all_pad():
@@ -142,11 +167,21 @@ def test_exact_activations_tp8_rank(rows):
     _exact_case(configs.TP8_RANK_MXFP4, rows, 70 + rows)
 
 
+def test_exact_activations_tp8_rank_ceil_rule():
+    _exact_case(configs.TP8_RANK_MXFP4.with_(name="tp8_rank_mxfp4_ceil", mx_scale_rule="ceil"), 8, 78)
+
+
 @pytest.mark.parametrize("rows", [1, 6, 16])
 def test_tp8_rank_mxfp4_normed_input(rows):
     """With a normed input both sides quantise the same bf16 x, so no code can flip: the
     strict element rule applies."""
     parity_case(configs.TP8_RANK_MXFP4_NORMED, rows, 51, dev=DEV)
+
+
+@pytest.mark.parametrize("rows", [5, 16])
+def test_tp8_rank_mxfp4_normed_input_ceil_rule_near_one(rows):
+    parity_case(configs.TP8_RANK_MXFP4_NORMED.with_(name="tp8_rank_mxfp4_normed_ceil", mx_scale_rule="ceil"),
+                rows, 53, stress=True, dev=DEV)
 
 
 def test_tiny_mxfp4_normed_input():

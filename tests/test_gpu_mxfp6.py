@@ -112,6 +112,11 @@ def test_tp8_rank_mxfp6(rows):
     parity_case(configs.TP8_RANK_MXFP6, rows, 41, dev=DEV)
 
 
+@pytest.mark.parametrize("rows", [2, 16])
+def test_tp8_rank_mxfp6_gated_norm_weight_near_one(rows):
+    parity_case(configs.TP8_RANK_MXFP6, rows, 46, stress=True, dev=DEV)
+
+
 def test_tp8_rank_mxfp6_all_pad():
     parity_case(configs.TP8_RANK_MXFP6, 3, 42, all_pad=True, dev=DEV)
 

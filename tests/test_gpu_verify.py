@@ -18,7 +18,7 @@ import torch
 from gated_deltanet_linear_decode_amd import configs, synth
 from gated_deltanet_linear_decode_amd.block import GdnBlock
 from oracle import gdn as og
-from tests.gpu_util import call_to, close, note, weights_to
+from tests.gpu_util import call_to, close, note, record, weights_to
 from tests.helpers import oracle_cfg, oracle_state, oracle_weights, u16
 
 pytestmark = pytest.mark.gpu
@@ -67,9 +67,9 @@ def _same(a, b, keys=("core", "residual", "conv_state", "ssm_state")):
         assert torch.equal(x, y), k
 
 
-def verify_case(shape, R, T, seed, flips=None, **kw):
-    note(f"verify {shape.name} R={R} T={T} seed={seed} {kw}")
-    w = synth.make_weights(shape, seed)
+def verify_case(shape, R, T, seed, flips=None, stress=False, **kw):
+    note(f"verify {shape.name} R={R} T={T} seed={seed} stress={stress} {kw}")
+    w = synth.make_weights(shape, seed, gated_norm_stress=stress)
     c = synth.make_call(shape, R * T, seed)
     src, dst = verify_indices(shape, R, T, seed, **kw)
     blk = GdnBlock(shape, max_rows=R * T, device=DEV)
@@ -79,7 +79,7 @@ def verify_case(shape, R, T, seed, flips=None, **kw):
     blk.close()
     ref = og.verify_block(oracle_cfg(shape), oracle_weights(w), u16(c.x), u16(c.residual), u16(c.conv_state),
                           oracle_state(c.ssm_state), src, dst)
-    label = f"{shape.name}/R{R}T{T}/s{seed}"
+    label = f"{shape.name}/R{R}T{T}/s{seed}" + ("/wg1" if stress else "")
     want_res = u16(c.residual) if ref["residual"] is None else ref["residual"]
     assert np.array_equal(u16(out["residual"]), want_res), f"{label}: residual differs"
     core = u16(out["core"])
@@ -96,6 +96,7 @@ def verify_case(shape, R, T, seed, flips=None, **kw):
         stats["conv"] = close(f"{label} conv", conv_g[written], ref["conv_state"][written], flips=flips)
         stats["ssm"] = close(f"{label} ssm", ssm_g[written], ref["ssm_state"][written],
                              bf16=shape.ssm_state_dtype == "bf16", flips=flips)
+    record(label, stats)
     note(f"  ok {stats}")
 
 
@@ -120,6 +121,18 @@ def test_tp8_rank_mxfp4_verify():
 
 def test_tp8_rank_mxfp6_normed_verify():
     verify_case(configs.TP8_RANK_MXFP6.with_(name="mx6_normed", input_normed=True, has_residual=False), 2, 4, 713)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tp8_rank_bf16_state_layer0", "tp8_rank_f32_state_pads"])
+def test_verify_gated_norm_weight_near_one(name):
+    """The w_g = 1 + N(0, 0.02) draw, so the core values are O(1) and the element bound
+    bites on them."""
+    shape = TINY_V if name == "tiny" else configs.ALL[name]
+    verify_case(shape, 3, 4, 714, stress=True)
+
+
+def test_tp8_rank_mxfp4_verify_gated_norm_weight_near_one():
+    verify_case(configs.TP8_RANK_MXFP4, 2, 4, 715, flips=(0.02, 0.15), stress=True)
 
 
 def _decode(blk, shape, wd, x, res, conv, ssm, idx):

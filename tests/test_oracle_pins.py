@@ -145,13 +145,14 @@ def test_bf16_projection_single_rounding_of_exact_sum():
     assert got[0, 0] == 1.0 + 0.0  # 1 + 2^-10 rounds to 1 in bf16
 
 
-def test_mxfp4_hand_worked_blocks():
-    fx = _golden("mxfp4_blocks.json")
+@pytest.mark.parametrize("rule", ["rounded_max", "ceil"])
+def test_mxfp4_hand_worked_blocks(rule):
+    fx = _golden("mxfp4_blocks.json")["rules"][rule]
     for blk in fx["blocks"]:
         v = np.zeros(32)
         for i, val in blk["values"].items():
             v[int(i)] = val
-        codes, scales = og.mxfp4_quantize(v)
+        codes, scales = og.mxfp4_quantize(v, rule)
         assert int(scales[0]) == blk["scale_byte"], blk["note"]
         want = np.zeros(32, dtype=np.uint8)
         for i, c in blk["codes"].items():
@@ -159,7 +160,27 @@ def test_mxfp4_hand_worked_blocks():
         assert np.array_equal(codes, want), blk["note"]
 
 
-def test_mxfp4_round_trip_on_representable_blocks():
+def test_mxfp4_scale_rules_differ_only_between_1_5_and_1_75():
+    """With the block maximum M 2^E (1 <= M < 2): both rules give E - 2 for M <= 1.5 and
+    E - 1 for M >= 1.75; between, the rounded maximum stays at E - 2 (its elements round
+    down to 6) while the ceiling moves up, so no element passes 6 times the scale."""
+    rng = np.random.default_rng(11)
+    E = rng.integers(-100, 100, 4000)
+    M = np.concatenate([rng.uniform(1.0, 2.0, 3000), [1.0, 1.5, 1.75, 1.9921875] * 250])
+    amax = M * np.exp2(E.astype(np.float64))
+    er = og.mx_block_exponent(amax, 1, "rounded_max")
+    ec = og.mx_block_exponent(amax, 1, "ceil")
+    assert np.array_equal(er, E - 2 + (M >= 1.75))
+    assert np.array_equal(ec, E - 2 + (M > 1.5))
+    assert np.all(amax <= 6.0 * np.exp2(ec.astype(np.float64)))
+    assert np.all(amax < 7.0 * np.exp2(er.astype(np.float64)))
+    # E2M3's three mantissa bits: a carry exactly from 1.1111b (the MXFP6 weights' rule)
+    e3 = og.mx_block_exponent(amax, 3, "rounded_max")
+    assert np.array_equal(e3, E - 2 + (M >= 1.9375))
+
+
+@pytest.mark.parametrize("rule", ["rounded_max", "ceil"])
+def test_mxfp4_round_trip_on_representable_blocks(rule):
     rng = np.random.default_rng(6)
     codes = rng.integers(0, 16, (5, 64)).astype(np.uint8)
     codes[:, 0] = 7                                # every block reaches 6 * 2^e
@@ -167,7 +188,7 @@ def test_mxfp4_round_trip_on_representable_blocks():
     codes[codes == 8] = 0                          # -0 quantises to +0
     scales = rng.integers(100, 140, (5, 2)).astype(np.uint8)
     v = og.mxfp4_dequantize(codes, scales)
-    c2, s2 = og.mxfp4_quantize(v)
+    c2, s2 = og.mxfp4_quantize(v, rule)
     assert np.array_equal(c2, codes) and np.array_equal(s2, scales)
 
 
