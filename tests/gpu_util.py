@@ -88,12 +88,15 @@ def error_stats(g, r, bf16):
     above 1e-5 relative; and ||gpu - oracle|| / ||oracle|| over the whole tensor."""
     err = np.abs(g - r)
     nr = np.linalg.norm(r)
+    rms = nr / np.sqrt(r.size) if r.size else 0.0
+    scale = np.maximum(np.abs(r), rms)  # an element's magnitude, at least the tensor's rms
     st = {"max_abs": float(err.max()), "rel_norm": float(np.linalg.norm(g - r) / nr) if nr > 0 else 0.0}
     if bf16:
         st["max_ulp"] = float((err / _ulp_bf16(r)).max())
+        st["ulp_at_scale"] = float((err / _ulp_bf16(scale)).max()) if rms > 0 else 0.0
         st["frac_diff"] = float((err > 0).mean())
     else:
-        rms = nr / np.sqrt(r.size) if r.size else 0.0
+        st["rel_at_scale"] = float((err / scale).max()) if rms > 0 else 0.0
         big = np.abs(r) > 1e-3 * rms
         rel = err[big] / np.abs(r[big]) if big.any() else np.zeros(1)
         st["max_rel"] = float(rel.max())
