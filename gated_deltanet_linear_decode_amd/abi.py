@@ -27,7 +27,7 @@ GDN_MAX_ROWS = 16
 EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error",
             "gdn_block_packed_weight_bytes", "gdn_block_pack_weights", "gdn_block_check",
             "gdn_mxfp4_quantize", "gdn_block_decode_with_out_proj", "gdn_mxfp6_round_weights",
-            "gdn_block_verify", "gdn_block_set_spin_limit")
+            "gdn_block_verify", "gdn_block_set_spin_limit", "gdn_block_decode_noalloc")
 
 
 class GdnBlockConfig(ctypes.Structure):
@@ -73,6 +73,9 @@ def load() -> ctypes.CDLL:
         lib.gdn_block_decode.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(GdnBlockWeights), c_void_p,
                                          c_void_p, c_void_p, c_int32, c_void_p, c_void_p]
         lib.gdn_block_decode.restype = c_int
+        lib.gdn_block_decode_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(GdnBlockWeights), c_void_p,
+                                                 c_void_p, c_void_p, c_int32, c_void_p, c_void_p]
+        lib.gdn_block_decode_noalloc.restype = c_int
         lib.gdn_block_destroy.argtypes = [c_void_p]
         lib.gdn_block_destroy.restype = None
         lib.gdn_block_last_error.argtypes = [c_void_p]
@@ -116,6 +119,14 @@ def gdn_block_decode(handle, x: int, residual: int, weights: GdnBlockWeights, co
                      ssm_state: int, state_idx: int, rows: int, core_out: int, stream: int) -> None:
     rc = load().gdn_block_decode(handle, x, residual, ctypes.byref(weights), conv_state, ssm_state,
                                  state_idx, rows, core_out, stream)
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(handle))
+
+
+def gdn_block_decode_noalloc(handle, x: int, residual: int, weights: GdnBlockWeights, conv_state: int,
+                             ssm_state: int, state_idx: int, rows: int, core_out: int, stream: int) -> None:
+    rc = load().gdn_block_decode_noalloc(handle, x, residual, ctypes.byref(weights), conv_state, ssm_state,
+                                         state_idx, rows, core_out, stream)
     if rc != GDN_OK:
         raise GdnError(rc, gdn_block_last_error(handle))
 

@@ -112,11 +112,12 @@ class GdnBlock:
         return abi.gdn_block_check(self.handle)
 
     def decode(self, x, residual, weights, conv_state, ssm_state, state_idx, core_out, rows=None,
-               stream=None, weights_struct=None, out=None):
+               stream=None, weights_struct=None, out=None, noalloc=False):
         """Enqueue one decode step on `stream` (default: torch's current stream).
 
         With a shape that folds out_proj, `out` ([R, H] bf16) receives the rank's out_proj
-        partial.
+        partial. With `noalloc` the step runs through gdn_block_decode_noalloc (the
+        library's fixed per-GPU scratch instead of the handle's).
 
         `weights` is a GdnWeights on the device, or pass a prepared
         `weights_struct` (from weights_struct()) to skip re-checking."""
@@ -138,6 +139,8 @@ class GdnBlock:
         if s.fold_out_proj:
             pout = _check(out, "out", torch.bfloat16, (R, H), d)
             abi.gdn_block_decode_with_out_proj(self.handle, px, pr, ws, pc, ps, pi, R, po, pout, stream)
+        elif noalloc:
+            abi.gdn_block_decode_noalloc(self.handle, px, pr, ws, pc, ps, pi, R, po, stream)
         else:
             abi.gdn_block_decode(self.handle, px, pr, ws, pc, ps, pi, R, po, stream)
 

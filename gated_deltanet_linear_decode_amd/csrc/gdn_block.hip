@@ -59,6 +59,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "gdn_block.h"
@@ -1509,8 +1510,30 @@ __global__ __launch_bounds__(kThreads) void mx_quant_kernel(const uint16_t* __re
 
 }  // namespace
 
+// The scratch of gdn_block_decode_noalloc: one fixed device array, which the code object
+// loader places on every GPU the library runs on (held until the process ends). The
+// hand-off counters take its first kStaticSyncBytes (the same offset for every handle, so
+// handles of different shapes can use it one after another: each launch leaves every
+// counter at zero); the activation image and the split partials follow. In host code the
+// array's name is not a device address: the address is looked up once per device
+// (static_scratch) and only that is passed to kernels and copies.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr size_t kStaticSyncBytes = size_t(64) << 10;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 // =======================================================================================
 // host side: the C ABI
+
+namespace {
+// the scratch pointers one launch uses: a handle's own allocation, or the static array
+struct Scratch {
+  uint16_t* xn;
+  uint32_t* xq;
+  uint32_t* xqs;
+  float* part;
+  uint32_t* sync;
+};
+}  // namespace
 
 struct gdn_block {
   gdn_block_config cfg;
@@ -1523,18 +1546,41 @@ struct gdn_block {
   int o, ko;          // out_proj workgroups (4 tiles of 16 columns of H each) and K (nv * dv)
   int fmt;            // kFmtBf16, kFmtMx4 or kFmtMx6 (the in_proj_qkvz format)
   bool mx;            // MXFP4: the activations are quantised too (a second scratch image)
-  void* scratch;
-  uint16_t* xn;
-  uint32_t* xq;
-  uint32_t* xqs;
-  float* part;
-  uint32_t* sync;
+  void* scratch;       // the handle's own allocation: [data | sync words]
+  size_t data_bytes;   // activation image and partials, at offsets o_* of a data base
+  size_t o_xn, o_part, o_xq, o_xqs;
+  Scratch own;
+  uint32_t* sync;      // == own.sync
   std::string err;
 };
 
 namespace {
 
 thread_local std::string g_create_error;
+
+// per device: the address of the static scratch array (null until looked up), or why the
+// lookup failed
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxDevices];
+std::string g_static_why[kMaxDevices];
+
+// Looks up (once per device, with that device current) the device address of the static
+// scratch array, and clears its counter lines, which must start at zero.
+void static_scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static_ptr[dev] || !g_static_why[dev].empty()) return;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e == hipSuccess) e = hipMemset(ptr, 0, kStaticSyncBytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess)
+    g_static_ptr[dev] = ptr;
+  else
+    g_static_why[dev] = std::string("the static scratch of device ") + std::to_string(dev) +
+                        " could not be set up: " + hipGetErrorString(e);
+}
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -1688,11 +1734,12 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
     off = align_up(off + bytes, 256);
     return o;
   };
-  const size_t o_xn = take((size_t)R * H * 2);
-  const size_t o_part = take((size_t)S * R * b->pw * 4);
+  b->o_xn = take((size_t)R * H * 2);
+  b->o_part = take((size_t)S * R * b->pw * 4);
+  b->o_xq = b->mx ? take((size_t)R * H / 2) : 0;
+  b->o_xqs = b->mx ? take((size_t)R * H / 32) : 0;
+  b->data_bytes = off;
   const size_t o_sync = take((size_t)b->sync_words * 4);
-  const size_t o_xq = b->mx ? take((size_t)R * H / 2) : 0;
-  const size_t o_xqs = b->mx ? take((size_t)R * H / 32) : 0;
 
   hipError_t e = hipGetDevice(&b->device);
   if (e == hipSuccess) e = hipMalloc(&b->scratch, off);
@@ -1705,11 +1752,14 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
     return GDN_E_HIP;
   }
   char* base = static_cast<char*>(b->scratch);
-  b->xn = reinterpret_cast<uint16_t*>(base + o_xn);
-  b->part = reinterpret_cast<float*>(base + o_part);
-  b->sync = reinterpret_cast<uint32_t*>(base + o_sync);
-  b->xq = b->mx ? reinterpret_cast<uint32_t*>(base + o_xq) : nullptr;
-  b->xqs = b->mx ? reinterpret_cast<uint32_t*>(base + o_xqs) : nullptr;
+  b->own.xn = reinterpret_cast<uint16_t*>(base + b->o_xn);
+  b->own.part = reinterpret_cast<float*>(base + b->o_part);
+  b->own.sync = reinterpret_cast<uint32_t*>(base + o_sync);
+  b->own.xq = b->mx ? reinterpret_cast<uint32_t*>(base + b->o_xq) : nullptr;
+  b->own.xqs = b->mx ? reinterpret_cast<uint32_t*>(base + b->o_xqs) : nullptr;
+  b->sync = b->own.sync;
+  // the set-up of gdn_block_decode_noalloc on this device (a failure is reported there)
+  static_scratch_setup(b->device);
   g_create_error.clear();
   *out = b;
   return GDN_OK;
@@ -1779,9 +1829,9 @@ extern "C" int gdn_block_pack_weights(gdn_block_t b, const gdn_block_weights* w,
 
 namespace {
 // one launch over `rows` sequences of `tokens` tokens each (decode: tokens = 1, dst_idx null)
-int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_weights* w, void* conv_state,
-                void* ssm_state, const int32_t* state_idx, const int32_t* dst_idx, int32_t rows, int32_t tokens,
-                void* core_out, void* out, void* stream) {
+int decode_impl(gdn_block* b, const Scratch& sc, const void* x, void* residual, const gdn_block_weights* w,
+                void* conv_state, void* ssm_state, const int32_t* state_idx, const int32_t* dst_idx, int32_t rows,
+                int32_t tokens, void* core_out, void* out, void* stream) {
   const gdn_block_config& c = b->cfg;
   if (tokens < 1 || tokens > c.max_rows)
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_verify: tokens must be in 1.." + std::to_string(c.max_rows) +
@@ -1852,11 +1902,11 @@ int decode_impl(gdn_block* b, const void* x, void* residual, const gdn_block_wei
   a.wo_pk = packed ? reinterpret_cast<const uint16_t*>(static_cast<const uint8_t*>(w->w_proj_packed) +
                                                        packed_qkvz_bytes(b) + packed_scale_bytes(b) + packed_ba_bytes(b))
                    : nullptr;
-  a.xn = b->xn;
-  a.xq = b->xq;
-  a.xqs = b->xqs;
-  a.part = b->part;
-  a.sync = b->sync;
+  a.xn = sc.xn;
+  a.xq = sc.xq;
+  a.xqs = sc.xqs;
+  a.part = sc.part;
+  a.sync = sc.sync;
   a.H = c.hidden;
   a.R = rows * tokens;
   a.Rs = rows;
@@ -1909,7 +1959,44 @@ extern "C" int gdn_block_decode(gdn_block_t b, const void* x, void* residual, co
   if (b->fold)
     return fail(b, GDN_E_INVALID_ARG,
                 "gdn_block_decode: this handle folds out_proj; call gdn_block_decode_with_out_proj");
-  return decode_impl(b, x, residual, w, conv_state, ssm_state, state_idx, nullptr, rows, 1, core_out, nullptr, stream);
+  return decode_impl(b, b->own, x, residual, w, conv_state, ssm_state, state_idx, nullptr, rows, 1, core_out, nullptr,
+                     stream);
+}
+
+extern "C" int gdn_block_decode_noalloc(gdn_block_t b, const void* x, void* residual, const gdn_block_weights* w,
+                                        void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
+                                        void* core_out, void* stream) {
+  if (!b) return GDN_E_INVALID_ARG;
+  if (b->fold)
+    return fail(b, GDN_E_INVALID_ARG,
+                "gdn_block_decode_noalloc: this handle folds out_proj; call gdn_block_decode_with_out_proj");
+  const int dev = b->device;
+  void* base = nullptr;
+  std::string why;
+  if (dev >= 0 && dev < kMaxDevices) {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    base = g_static_ptr[dev];
+    why = g_static_why[dev];
+  }
+  if (!base)
+    return fail(b, GDN_E_HIP, "gdn_block_decode_noalloc: " +
+                                  (why.empty() ? "no static scratch on device " + std::to_string(dev) : why));
+  const size_t sync_bytes = (size_t)b->sync_words * 4;
+  if (sync_bytes > kStaticSyncBytes || b->data_bytes > kStaticScratchBytes - kStaticSyncBytes)
+    return fail(b, GDN_E_UNSUPPORTED,
+                "gdn_block_decode_noalloc: this handle needs " + std::to_string(b->data_bytes) + " bytes of scratch and " +
+                    std::to_string(sync_bytes) + " bytes of counters (max_rows " + std::to_string(b->cfg.max_rows) +
+                    "); the static scratch holds " + std::to_string(kStaticScratchBytes - kStaticSyncBytes) + " and " +
+                    std::to_string(kStaticSyncBytes) + ": create the handle with a smaller max_rows");
+  char* data = static_cast<char*>(base) + kStaticSyncBytes;
+  Scratch sc;
+  sc.sync = static_cast<uint32_t*>(base);
+  sc.xn = reinterpret_cast<uint16_t*>(data + b->o_xn);
+  sc.part = reinterpret_cast<float*>(data + b->o_part);
+  sc.xq = b->mx ? reinterpret_cast<uint32_t*>(data + b->o_xq) : nullptr;
+  sc.xqs = b->mx ? reinterpret_cast<uint32_t*>(data + b->o_xqs) : nullptr;
+  return decode_impl(b, sc, x, residual, w, conv_state, ssm_state, state_idx, nullptr, rows, 1, core_out, nullptr,
+                     stream);
 }
 
 extern "C" int gdn_block_decode_with_out_proj(gdn_block_t b, const void* x, void* residual, const gdn_block_weights* w,
@@ -1919,7 +2006,8 @@ extern "C" int gdn_block_decode_with_out_proj(gdn_block_t b, const void* x, void
   if (!b->fold)
     return fail(b, GDN_E_INVALID_ARG,
                 "gdn_block_decode_with_out_proj: this handle was created without fold_out_proj");
-  return decode_impl(b, x, residual, w, conv_state, ssm_state, state_idx, nullptr, rows, 1, core_out, out, stream);
+  return decode_impl(b, b->own, x, residual, w, conv_state, ssm_state, state_idx, nullptr, rows, 1, core_out, out,
+                     stream);
 }
 
 extern "C" int gdn_block_verify(gdn_block_t b, const void* x, void* residual, const gdn_block_weights* w,
@@ -1929,23 +2017,30 @@ extern "C" int gdn_block_verify(gdn_block_t b, const void* x, void* residual, co
   if (!dst_idx) return fail(b, GDN_E_INVALID_ARG, "gdn_block_verify: dst_idx must not be NULL");
   if (b->fold)
     return fail(b, GDN_E_INVALID_ARG, "gdn_block_verify: not for a handle that folds out_proj");
-  return decode_impl(b, x, residual, w, conv_state, ssm_state, src_idx, dst_idx, rows, tokens, core_out, nullptr,
-                     stream);
+  return decode_impl(b, b->own, x, residual, w, conv_state, ssm_state, src_idx, dst_idx, rows, tokens, core_out,
+                     nullptr, stream);
 }
 
 extern "C" int gdn_block_check(gdn_block_t b, uint32_t* error_word) {
   if (!b || !error_word) return GDN_E_INVALID_ARG;
-  uint32_t v = 0;
-  uint32_t* word = b->sync + (size_t)kSyError * kLine;
+  void* st = nullptr;  // the static scratch of the handle's device, once set up
+  if (b->device >= 0 && b->device < kMaxDevices) {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    st = g_static_ptr[b->device];
+  }
+  uint32_t v = 0, vs = 0;
   // every enqueued launch has ended, on every stream of the device
   hipError_t e = hipDeviceSynchronize();
-  if (e == hipSuccess) e = hipMemcpy(&v, word, 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(&v, b->sync + (size_t)kSyError * kLine, 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && st)
+    e = hipMemcpy(&vs, static_cast<uint32_t*>(st) + (size_t)kSyError * kLine, 4, hipMemcpyDeviceToHost);
   // A launch whose wait gave up may have left hand-off counters uncleared (their
   // clearing assumes that every workgroup arrived): clear all of them, and the word.
   if (e == hipSuccess && v) e = hipMemset(b->sync, 0, (size_t)b->sync_words * 4);
-  if (e == hipSuccess && v) e = hipDeviceSynchronize();
+  if (e == hipSuccess && vs) e = hipMemset(st, 0, kStaticSyncBytes);
+  if (e == hipSuccess && (v || vs)) e = hipDeviceSynchronize();
   if (e != hipSuccess) return fail(b, GDN_E_HIP, std::string("gdn_block_check: ") + hipGetErrorString(e));
-  *error_word = v;
+  *error_word = v | vs;
   return GDN_OK;
 }
 

@@ -181,6 +181,27 @@ int gdn_block_decode(gdn_block_t blk, const void* x, void* residual, const gdn_b
                      void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
                      void* core_out, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): gdn_block_decode, same arguments and
+ * results, bit for bit, with the launch's scratch (the hand-off counters, the activation
+ * image and the projection partials) taken from a fixed device array that the library
+ * holds on each GPU it runs on until the process ends, instead of the handle's own
+ * scratch. The array is 8 MiB: 64 KiB of counter lines (at the same place for every
+ * handle) and 8128 KiB of data. A handle whose scratch does not fit (a large hidden size
+ * or head count at a large max_rows; the TP8-rank and full-width dense shapes fit at
+ * max_rows 16) is refused with GDN_E_UNSUPPORTED and both sizes in the message. Its
+ * address is looked up (and its counters cleared) once per device by gdn_block_create;
+ * if that failed, this call returns GDN_E_HIP with the reason. This call allocates
+ * nothing and enqueues one launch. Every such call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other handles, other threads)
+ * race and give undefined results; calls ordered on one stream are fine, whatever their
+ * handles. Each launch that completes normally leaves the counters at zero; after a
+ * wait gives up, gdn_block_check on any handle of that GPU clears them. Not for a
+ * handle with fold_out_proj. */
+int gdn_block_decode_noalloc(gdn_block_t blk, const void* x, void* residual, const gdn_block_weights* w,
+                             void* conv_state, void* ssm_state, const int32_t* state_idx, int32_t rows,
+                             void* core_out, void* stream);
+
 /* gdn_block_decode, plus the rank's out_proj partial: out [rows, H] bf16 (device,
  * 16-byte aligned) = bf16(core_out W_out^T) with the sum in f32, one output row per
  * input row (a pad row's partial is zero). Only for a handle created with
@@ -253,8 +274,9 @@ int gdn_mxfp6_round_weights(const void* w, int32_t rows, int32_t cols, void* cod
  * Such a launch can also leave the hand-off counters in the handle's scratch uncleared
  * (each launch clears them on the assumption that every workgroup arrived), which would
  * corrupt the handle's next decodes: when the word is not 0, this call also clears every
- * counter, so decodes enqueued after it start clean. 0 means every decode since the
- * last check completed normally. */
+ * counter, so decodes enqueued after it start clean. The word of the handle's device's
+ * gdn_block_decode_noalloc scratch is read, ORed in and cleared the same way. 0 means
+ * every decode since the last check completed normally. */
 int gdn_block_check(gdn_block_t blk, uint32_t* error_word);
 
 /* Set the poll limit of every bounded wait in this handle's later decodes (default

@@ -45,11 +45,12 @@ def call_to(c: GdnCall, dev) -> GdnCall:
     return GdnCall(**{k: v.to(dev).contiguous() for k, v in c.__dict__.items()})
 
 
-def run_gpu(blk: GdnBlock, shape, wd: GdnWeights, cd: GdnCall, rows=None, packed=None, check=True):
+def run_gpu(blk: GdnBlock, shape, wd: GdnWeights, cd: GdnCall, rows=None, packed=None, check=True, noalloc=False):
     """Run one decode on copies of the device inputs; returns CPU tensors.
 
     `packed`: None streams the row-major weights; a tensor from blk.pack() streams
-    the tiled copy. With `check`, the handle's sticky error word must stay 0."""
+    the tiled copy. With `check`, the handle's sticky error word must stay 0. With
+    `noalloc`, the decode goes through gdn_block_decode_noalloc."""
     R = cd.x.shape[0] if rows is None else rows
     res = cd.residual.clone()
     conv = cd.conv_state.clone()
@@ -58,7 +59,7 @@ def run_gpu(blk: GdnBlock, shape, wd: GdnWeights, cd: GdnCall, rows=None, packed
     out = (torch.full((R, shape.hidden), float("nan"), dtype=torch.bfloat16, device=cd.x.device)
            if shape.fold_out_proj else None)
     ws = blk.packed_struct(wd, packed) if packed is not None else blk.weights_struct(wd)
-    blk.decode(cd.x, res, None, conv, ssm, cd.state_idx, core, weights_struct=ws, out=out)
+    blk.decode(cd.x, res, None, conv, ssm, cd.state_idx, core, weights_struct=ws, out=out, noalloc=noalloc)
     torch.cuda.synchronize()
     if check:
         assert blk.check() == 0, "a wait inside the decode gave up"
