@@ -203,11 +203,13 @@ __device__ unsigned long long g_trace[kTraceBlocks * kTraceSlots];
 #endif
 
 // sync word lines (one 128-byte line each): norm workgroups done (kNormCopies copies,
-// polled spread out); b|a tile splits done; recurrence workgroups finished; the sticky
-// error word; norm workgroups finished; out_proj workgroups past their wait and (on
-// kCoreCopies lines) recurrence workgroups whose core rows are stored (out_proj fold);
-// then per key-head group, on kGroupCopies lines: tile splits done; then per (sequence,
-// key-head group): value heads that have read the old q|k conv rows.
+// polled spread out; the MXFP4 path); b|a tile splits done; recurrence workgroups
+// finished; the sticky error word; norm workgroups finished; out_proj workgroups past
+// their wait and (on kCoreCopies lines) recurrence workgroups whose core rows are stored
+// (out_proj fold); each row's rstd, on kNormCopies lines (word r of a line is row r's
+// rstd, 0 until published); projection workgroups holding their residual slice, on
+// kNormCopies lines; then per key-head group, on kGroupCopies lines: tile splits done;
+// then per (sequence, key-head group): value heads that have read the old q|k conv rows.
 enum {
   kSyNorm = 0,
   kSyBa = kNormCopies,
@@ -217,7 +219,9 @@ enum {
   kSyOutExit,  // top line of the out_proj workgroups' two-level exit count
   kSyCoreDone,
   kSyOutExit1 = kSyCoreDone + kCoreCopies,  // its first level, kCoreCopies lines
-  kSyGroup0 = kSyOutExit1 + kCoreCopies
+  kSyRstd = kSyOutExit1 + kCoreCopies,
+  kSyLoaded = kSyRstd + kNormCopies,
+  kSyGroup0 = kSyLoaded + kNormCopies
 };
 enum : uint32_t { kErrNormWait = 1u, kErrGroupWait = 2u, kErrConvWait = 4u };
 
@@ -318,6 +322,88 @@ __device__ __forceinline__ uint32_t mx_quant8(const uint32_t* v, uint32_t& ebyte
   }
   ebyte = (uint32_t)(e + 127);
   return codes;
+}
+
+// Without MXFP4 (bf16 or MXFP6 in_proj_qkvz): one workgroup per row loads the whole row,
+// forms h = bf16(x + residual) and the row's rstd, and publishes only rstd, as the data
+// itself: word `row` of kNormCopies lines, 0 until written (rstd is never 0). Projection
+// workgroups load the x (and residual) slice of their own K range at launch and form xn
+// from it with the same arithmetic once rstd is there, so no xn row makes a round trip
+// through memory ("vLLM PR #60833", Details: x is not held in LDS; rstd is handed off).
+// The residual row is then rewritten with h: with a residual input, only once every
+// projection workgroup holds its residual slice.
+__device__ void norm_rstd_role(const Args& a, int row, float* red) {
+  const int H = a.H, nchunk = H >> 3, tid = threadIdx.x;
+  const uint4* xp = reinterpret_cast<const uint4*>(a.x + (size_t)row * H);
+  uint4* rp = reinterpret_cast<uint4*>(a.residual + (size_t)row * H);
+  uint4 hv[kNormMaxChunks], rv[kNormMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kNormMaxChunks; ++c) {  // every load of the row is issued up front
+    const int i = tid + c * kThreads;
+    if (i < nchunk) hv[c] = xp[i];
+  }
+  if (a.has_res) {
+#pragma unroll
+    for (int c = 0; c < kNormMaxChunks; ++c) {
+      const int i = tid + c * kThreads;
+      if (i < nchunk) rv[c] = rp[i];
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kNormMaxChunks; ++c) {
+    const int i = tid + c * kThreads;
+    if (i < nchunk) {
+      if (a.has_res) {
+        uint32_t* pv = reinterpret_cast<uint32_t*>(&hv[c]);
+        const uint32_t* pb = reinterpret_cast<const uint32_t*>(&rv[c]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          pv[k] = f2bf2(bf2f((uint16_t)pv[k]) + bf2f((uint16_t)pb[k]),
+                        bf2f((uint16_t)(pv[k] >> 16)) + bf2f((uint16_t)(pb[k] >> 16)));
+      }
+      const uint32_t* ph = reinterpret_cast<const uint32_t*>(&hv[c]);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float l = bf2f((uint16_t)ph[k]), h = bf2f((uint16_t)(ph[k] >> 16));
+        ss = fmaf(l, l, ss);
+        ss = fmaf(h, h, ss);
+      }
+    }
+  }
+  ss = block_sum(ss, red);
+  TRACE_POINT(1);
+  const float rstd = 1.0f / sqrtf(ss / (float)H + a.eps);
+  if (tid < kNormCopies) st_agent(reinterpret_cast<float*>(sy(a, kSyRstd + tid)) + row, rstd);
+  TRACE_POINT(2);
+  if (a.has_res) {
+    // every projection workgroup has counted itself on line gb % kNormCopies once it holds
+    // its residual slice: lane c of the first wave waits for line c's share
+    if (threadIdx.x < 64) {
+      const int c = threadIdx.x;
+      const int share = c < kNormCopies ? max(0, (a.G - c + kNormCopies - 1) / kNormCopies) : 0;
+      uint32_t* ctr = sy(a, kSyLoaded + (c < kNormCopies ? c : 0));
+      int it = 0;
+      while (!__all(share == 0 || ld_agent(ctr) >= (uint32_t)share)) {
+        __builtin_amdgcn_s_sleep(8);
+        if (++it > a.spin) {
+          if (c == 0) __hip_atomic_fetch_or(sy(a, kSyError), kErrNormWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    asm volatile("" ::: "memory");
+  }
+#pragma unroll
+  for (int c = 0; c < kNormMaxChunks; ++c) {
+    const int i = tid + c * kThreads;
+    if (i < nchunk) rp[i] = hv[c];
+  }
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) add_agent(sy(a, kSyNormExit), 1u);
+  TRACE_POINT(3);
 }
 
 template <bool MX>
@@ -567,6 +653,91 @@ __device__ __forceinline__ void xin_store(const Args& a, const XnIn& in, ProjSha
   __syncthreads();
   TRACE_POINT(1);
 }
+// Without MXFP4 the norm hands off only each row's rstd (norm_rstd_role). A projection
+// workgroup loads the x slice [0, R) x [k0, k0 + Kr) (and the residual slice) and its slice
+// of the norm weight at launch, before its weight loads, in the chunk mapping of
+// xin_issue; stage_h turns them into the xn slice in LDS.
+struct HIn {
+  XnIn x, r;
+  u32x4_t w;  // norm weight of this thread's 8 columns
+};
+__device__ __forceinline__ void hin_issue(const Args& a, int k0, HIn& in) {
+  const int cpr = a.Kr >> 3, rpp = kThreads / cpr, r0 = threadIdx.x / cpr, q = threadIdx.x - r0 * cpr;
+  if (r0 >= rpp) return;
+#pragma unroll
+  for (int u = 0; u < kXnChunks; ++u) {
+    const int row = r0 + u * rpp;
+    if (row < a.R) in.x.v[u] = *reinterpret_cast<const u32x4_t*>(a.x + (size_t)row * a.H + k0 + 8 * q);
+  }
+  if (a.has_res) {
+#pragma unroll
+    for (int u = 0; u < kXnChunks; ++u) {
+      const int row = r0 + u * rpp;
+      if (row < a.R) in.r.v[u] = *reinterpret_cast<const u32x4_t*>(a.residual + (size_t)row * a.H + k0 + 8 * q);
+    }
+  }
+  in.w = *reinterpret_cast<const u32x4_t*>(a.norm_w + k0 + 8 * q);
+}
+// h = bf16(x + residual) (or x) into LDS; with a residual input the workgroup then counts
+// itself as holding its residual slice (the LDS writes need the loaded data, so after the
+// barrier every load of the slice has returned); waits for the rows' rstd; and converts
+// its chunks to xn = bf16(h * rstd * (1 + w)) in place, the norm's own arithmetic.
+__device__ __forceinline__ void stage_h(const Args& a, int gb, const HIn& in, ProjShared& sh) {
+  const int cpr = a.Kr >> 3, rpp = kThreads / cpr, r0 = threadIdx.x / cpr, q = threadIdx.x - r0 * cpr;
+  const bool on = r0 < rpp;
+#pragma unroll
+  for (int u = 0; u < kXnChunks; ++u) {
+    const int row = r0 + u * rpp;
+    if (on && row < a.R) {
+      u32x4_t h = in.x.v[u];
+      if (a.has_res) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          h[k] = f2bf2(bf2f((uint16_t)h[k]) + bf2f((uint16_t)in.r.v[u][k]),
+                       bf2f((uint16_t)(h[k] >> 16)) + bf2f((uint16_t)(in.r.v[u][k] >> 16)));
+      }
+      *reinterpret_cast<u32x4_t*>(&sh.xs[row][8 * q]) = h;
+    }
+  }
+  __syncthreads();
+  if (a.has_res && threadIdx.x == 0) add_agent(sy(a, kSyLoaded + gb % kNormCopies), 1u);
+  // the rows' rstd: lane r of the first wave polls word r of line gb % kNormCopies
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    const float* line = reinterpret_cast<const float*>(sy(a, kSyRstd + gb % kNormCopies));
+    float v = 1.0f;
+    int it = 0;
+    while (true) {
+      if (l < a.R) v = ld_agent(line + l);
+      if (__all(v != 0.0f)) break;
+      __builtin_amdgcn_s_sleep(4);
+      if (++it > a.spin) {
+        if (l == 0) __hip_atomic_fetch_or(sy(a, kSyError), kErrNormWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    if (l < a.R) sh.red[0][l] = v;
+  }
+  __syncthreads();
+  TRACE_POINT(1);
+#pragma unroll
+  for (int u = 0; u < kXnChunks; ++u) {
+    const int row = r0 + u * rpp;
+    if (on && row < a.R) {
+      const float rstd = sh.red[0][row];
+      u32x4_t* p = reinterpret_cast<u32x4_t*>(&sh.xs[row][8 * q]);
+      const u32x4_t h = *p;
+      u32x4_t o;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        o[k] = f2bf2(bf2f((uint16_t)h[k]) * rstd * (1.0f + bf2f((uint16_t)in.w[k])),
+                     bf2f((uint16_t)(h[k] >> 16)) * rstd * (1.0f + bf2f((uint16_t)(in.w[k] >> 16))));
+      *p = o;
+    }
+  }
+  __syncthreads();
+}
+
 // MXFP4: wave w takes the (row, 512-wide unit) pairs w, w + 4, ...; lane l the chunk
 // unit * 64 + l of the pair's row, so a wave's 64 chunks are one unit (the quantiser's
 // layout: 4 lanes per 32-block, 16 blocks per unit)
@@ -605,7 +776,7 @@ __device__ __forceinline__ void xqin_store(const Args& a, const XnIn& in, ProjSh
 
 // bf16 tiles over the K range [s Kr, (s+1) Kr): with TILES, wave w streams tile t0 + w over
 // the whole range; otherwise the 4 waves stream tile t0, a quarter of the range each
-template <bool PACKED, bool TILES>
+template <bool PACKED, bool TILES, bool RS>
 __device__ void proj_bf16(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = TILES ? t0 + wave : t0;
@@ -620,7 +791,11 @@ __device__ void proj_bf16(const Args& a, int gb, int t0, int s, ProjShared& sh) 
   auto lstep = [&](int i) { return l0 + (i + rot < nsteps ? i + rot : i + rot - nsteps); };
 
   XnIn xi;
-  if (a.normed) xin_issue(a, s * a.Kr, xi);
+  HIn hi;
+  if (a.normed)
+    xin_issue(a, s * a.Kr, xi);
+  else if (RS)
+    hin_issue(a, s * a.Kr, hi);
   // weight window: step i lives in register set i % kWin until consumed
   u32x4_t w[kWin];
 #pragma unroll
@@ -629,6 +804,8 @@ __device__ void proj_bf16(const Args& a, int gb, int t0, int s, ProjShared& sh) 
 
   if (a.normed)
     xin_store(a, xi, sh);
+  else if (RS)
+    stage_h(a, gb, hi, sh);
   else
     stage_xn(a, gb, s * a.Kr, sh);
   const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
@@ -829,7 +1006,11 @@ __device__ void proj_mx6(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   const int rot = (t * 7 + s * 3) % ng;   // spread concurrent streams over the channels
   auto lgrp = [&](int m) { return m + rot < ng ? m + rot : m + rot - ng; };
   XnIn xi;
-  if (a.normed) xin_issue(a, s * a.Kr, xi);
+  HIn hi;
+  if (a.normed)
+    xin_issue(a, s * a.Kr, xi);
+  else
+    hin_issue(a, s * a.Kr, hi);
   Mx6Group w[kGrp6];
 #pragma unroll
   for (int m = 0; m < kGrp6; ++m)
@@ -838,7 +1019,7 @@ __device__ void proj_mx6(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   if (a.normed)
     xin_store(a, xi, sh);
   else
-    stage_xn(a, gb, s * a.Kr, sh);
+    stage_h(a, gb, hi, sh);
   const int xrow = min(lane & 15, a.R - 1);  // decode rows past R are clamped; never stored
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -889,10 +1070,10 @@ __device__ void proj_role(const Args& a, int gb, ProjShared& sh) {
     else if (FMT == kFmtMx6)
       proj_mx6<PACKED>(a, gb, 4 * tg, s, sh);
     else
-      proj_bf16<PACKED, true>(a, gb, 4 * tg, s, sh);
+      proj_bf16<PACKED, true, true>(a, gb, 4 * tg, s, sh);
   } else {
     const int g = gb - a.Gq, tb = g / a.S, s = g - tb * a.S;
-    proj_bf16<PACKED, false>(a, gb, a.Tq + tb, s, sh);
+    proj_bf16<PACKED, false, FMT != kFmtMx4>(a, gb, a.Tq + tb, s, sh);
   }
 }
 
@@ -1256,21 +1437,29 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
     if (tid < kCoreCopies) add_agent(sy(a, kSyCoreDone + tid), 1u);
   }
 
-  // The last recurrence workgroup past its waits clears the counters for the next launch:
-  // by then every projection tile has been counted (each group and the b|a tiles had a
-  // waiter), so every projection workgroup is past its norm wait, and no recurrence
-  // workgroup reads a counter again (the q|k conv counter is cleared by its owner).
-  if (tid == 128 && exit_ticket == (uint32_t)(a.Rs * a.nv - 1)) {
-    // the norm workgroups may still be rewriting residual rows (past their last wait)
-    int it = 0;
-    while (ld_agent(sy(a, kSyNormExit)) < (uint32_t)(a.R * a.P) && ++it <= a.spin) __builtin_amdgcn_s_sleep(4);
-    if (it > a.spin) __hip_atomic_fetch_or(sy(a, kSyError), kErrNormWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    st_agent(sy(a, kSyNormExit), 0u);
-    for (int c = 0; c < kNormCopies; ++c) st_agent(sy(a, kSyNorm + c), 0u);
-    st_agent(sy(a, kSyBa), 0u);
-    for (int g = 0; g < a.nk; ++g)
-      for (int c = 0; c < kGroupCopies; ++c) st_agent(sy(a, sy_group(g, c)), 0u);
-    st_agent(sy(a, kSyExit), 0u);
+  // The last recurrence workgroup past its waits clears the counters for the next launch
+  // (its third wave, which holds the exit ticket in lane 0): by then every projection tile
+  // has been counted (each group and the b|a tiles had a waiter), so every projection
+  // workgroup is past its norm (or rstd) wait, and no recurrence workgroup reads a counter
+  // again (the q|k conv counter is cleared by its owner).
+  if ((tid >> 6) == 2 && __shfl((int)exit_ticket, 0, 64) == a.Rs * a.nv - 1) {
+    const int l = tid & 63;
+    if (l == 0) {  // the norm workgroups may still be rewriting residual rows (past their last wait)
+      int it = 0;
+      while (ld_agent(sy(a, kSyNormExit)) < (uint32_t)(a.R * a.P) && ++it <= a.spin) __builtin_amdgcn_s_sleep(4);
+      if (it > a.spin) __hip_atomic_fetch_or(sy(a, kSyError), kErrNormWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (l < kNormCopies) {
+      st_agent(sy(a, kSyNorm + l), 0u);
+      st_agent(sy(a, kSyLoaded + l), 0u);
+      for (int r = 0; r < a.R; ++r) st_agent(sy(a, kSyRstd + l) + r, 0u);
+    }
+    for (int i = l; i < a.nk * kGroupCopies; i += 64) st_agent(sy(a, kSyGroup0 + i), 0u);
+    if (l == 0) {
+      st_agent(sy(a, kSyNormExit), 0u);
+      st_agent(sy(a, kSyBa), 0u);
+      st_agent(sy(a, kSyExit), 0u);
+    }
   }
   TRACE_POINT(4);
 }
@@ -1372,7 +1561,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   TRACE_POINT(0);
   const int nn = a.R * a.P, nr = a.Rs * a.nv;
   if (b < nn) {
-    norm_role<FMT == kFmtMx4>(a, b, sh.rec.bsum);
+    if (FMT == kFmtMx4)
+      norm_role<true>(a, b, sh.rec.bsum);
+    else
+      norm_rstd_role(a, b, sh.rec.bsum);
   } else if (b < nn + a.G) {
     proj_role<PACKED, FMT>(a, b - nn, sh.proj);
   } else if (b < nn + a.G + nr) {
@@ -1913,7 +2105,9 @@ int decode_impl(gdn_block* b, const Scratch& sc, const void* x, void* residual, 
   a.Tk = tokens;
   a.has_res = c.has_residual;
   a.normed = normed ? 1 : 0;
-  a.P = normed ? 0 : (c.hidden / 8 + kThreads - 1) / kThreads;
+  // norm workgroups per row: the MXFP4 image is made by ceil(H / 2048) of them, 2048 columns
+  // each; otherwise one publishes the row's rstd
+  a.P = normed ? 0 : b->fmt == kFmtMx4 ? (c.hidden / 8 + kThreads - 1) / kThreads : 1;
   a.T = b->t;
   a.Tq = b->tq;
   a.Tb = b->tb;

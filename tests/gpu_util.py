@@ -1,10 +1,22 @@
 """Shared pieces of the GPU tests: moving a synthetic call to the device,
 running the HIP block through the C ABI, and the parity rule.
 
-Parity rule for floating-point outputs (bf16 core, conv state, SSM state):
-|gpu - oracle| <= max(2e-2, one bf16 ulp of the oracle value) element by
-element, and cosine >= 0.9999 over the written elements. The residual, pad
-rows and untouched slots are compared bit for bit.
+Parity rule for floating-point outputs (bf16 core, conv state, out_proj partial, SSM
+state), over the written elements of each tensor, with scale = max(|oracle value|, the
+tensor's rms):
+  outer floor (every tensor): |gpu - oracle| <= max(2e-2, one bf16 ulp of the oracle
+    value) element by element, and cosine >= 0.9999;
+  bf16 tensors: |gpu - oracle| <= 4 bf16 ulps of the scale, and
+    ||gpu - oracle|| / ||oracle|| <= 4e-3;
+  the f32 SSM state: |gpu - oracle| <= 1.5e-2 * scale, and
+    ||gpu - oracle|| / ||oracle|| <= 3e-4.
+The tight bounds are set with a margin of 2-4 over the largest errors measured on
+MI355X over every GPU test case (2 ulps at scale and 1.4e-3 for the bf16 tensors; 5.6e-3
+at scale and 7.2e-5 for the f32 state): a correct kernel differs from the oracle by the
+f32-versus-f64 rounding of its sums, and where that moves a bf16 value by one ulp
+(projection outputs, conv outputs, o) the change spreads through the rest of the head.
+A uniform relative error of 1 % fails the norm bounds of both. The residual, pad rows and
+untouched slots are compared bit for bit.
 """
 import json
 import os
@@ -20,6 +32,11 @@ from tests.helpers import oracle_state, run_oracle, u16
 
 ABS_TOL = 2e-2
 COS_MIN = 0.9999
+ULPS_AT_SCALE = 4         # bf16 tensors: element bound in bf16 ulps of max(|oracle|, rms)
+REL_NORM_BF16 = 4e-3      # bf16 tensors: ||gpu - oracle|| / ||oracle||
+REL_AT_SCALE_F32 = 1.5e-2  # f32 state: element bound relative to max(|oracle|, rms)
+REL_NORM_F32 = 3e-4       # f32 state: ||gpu - oracle|| / ||oracle||
+FLIP_NORM_FACTOR = 10     # the norm bounds under the MXFP4 code-flip allowance
 
 
 def note(msg):
@@ -106,12 +123,14 @@ def error_stats(g, r, bf16):
 
 
 def close(name, got, ref, bf16=True, flips=None):
-    """Assert the parity rule; returns the tensor's measured error (error_stats) with the
-    counts above ABS_TOL ("n_abs") and outside the element bound ("n_bad").
+    """Assert the parity rule (see the module docstring); returns the tensor's measured
+    error (error_stats) with the counts above ABS_TOL ("n_abs") and outside either element
+    bound ("n_bad").
 
-    `flips` = (fraction, cap) relaxes the element rule for outputs downstream of the
-    MXFP4 activation quantiser: up to `fraction` of the elements may leave the bound, each
-    by at most `cap` (see tests/test_gpu_mxfp4.py for why); the cosine rule still holds."""
+    `flips` = (fraction, cap) relaxes the element rules for outputs downstream of the
+    MXFP4 activation quantiser: up to `fraction` of the elements may leave the bounds, each
+    by at most `cap`, and the norm bound is FLIP_NORM_FACTOR times wider (see
+    tests/test_gpu_mxfp4.py for why); the cosine rule still holds."""
     g = og.bf16_to_f64(got) if bf16 else np.asarray(got, np.float64)
     r = og.bf16_to_f64(ref) if bf16 else np.asarray(ref, np.float64)
     g, r = g.reshape(-1), r.reshape(-1)
@@ -119,7 +138,14 @@ def close(name, got, ref, bf16=True, flips=None):
         return {}
     assert np.all(np.isfinite(g)), f"{name}: non-finite values"
     err = np.abs(g - r)
-    bound = np.maximum(ABS_TOL, _ulp_bf16(r)) if bf16 else np.full_like(r, ABS_TOL)
+    nr = np.linalg.norm(r)
+    scale = np.maximum(np.abs(r), nr / np.sqrt(r.size))
+    if bf16:
+        bound = np.minimum(np.maximum(ABS_TOL, _ulp_bf16(r)), ULPS_AT_SCALE * _ulp_bf16(scale))
+        norm_bound = REL_NORM_BF16
+    else:
+        bound = np.minimum(ABS_TOL, REL_AT_SCALE_F32 * scale)
+        norm_bound = REL_NORM_F32
     bad = err > bound
     worst = (f"worst err {err.max():.4g} at {np.argmax(err)} (gpu {g[np.argmax(err)]}, "
              f"oracle {r[np.argmax(err)]})")
@@ -129,10 +155,13 @@ def close(name, got, ref, bf16=True, flips=None):
         frac, cap = flips
         assert bad.sum() <= frac * err.size, f"{name}: {bad.sum()} of {err.size} outside the bound; {worst}"
         assert err.max() <= cap, f"{name}: an error above the cap {cap}; {worst}"
-    nr, ng = np.linalg.norm(r), np.linalg.norm(g)
+    ng = np.linalg.norm(g)
     if nr > 0:
         cos = float(g @ r / (nr * ng))
         assert cos >= COS_MIN, f"{name}: cosine {cos}"
+        rel = float(np.linalg.norm(g - r) / nr)
+        nb = norm_bound * (FLIP_NORM_FACTOR if flips is not None else 1)
+        assert rel <= nb, f"{name}: ||gpu - oracle|| / ||oracle|| = {rel:.3g} above {nb:.3g}"
     st = error_stats(g, r, bf16)
     st["n_abs"], st["n_bad"] = int((err > ABS_TOL).sum()), int(bad.sum())
     return st
