@@ -178,14 +178,14 @@ __device__ __forceinline__ void wait_count(uint32_t* ctr, uint32_t target, uint3
 // In-kernel timeline for profiling builds (-DGDN_TRACE): thread 0 of each workgroup stamps
 // the 100 MHz wall clock at up to kTraceSlots points of its role. Compiled out otherwise.
 #ifdef GDN_TRACE
-constexpr int kTraceSlots = 8;
+constexpr int kTraceSlots = 16;
 constexpr int kTraceBlocks = 8192;
 __device__ unsigned long long g_trace[kTraceBlocks * kTraceSlots];
 #define TRACE_POINT(k)                                                                          \
   do {                                                                                          \
     if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks) g_trace[blockIdx.x * kTraceSlots + (k)] = wall_clock64(); \
   } while (0)
-// slot k <- (XCC id << 16) | hardware id word (CU, SE, ...) of the wave
+// slot k <- (XCC id << 32) | hardware id word (CU, SE, ...) of the wave
 #define TRACE_HWID(k)                                                                           \
   do {                                                                                          \
     if (threadIdx.x == 0 && blockIdx.x < kTraceBlocks)                                          \
@@ -829,7 +829,7 @@ __device__ void proj_bf16(const Args& a, int gb, int t0, int s, ProjShared& sh) 
   else
     publish_reduced(a, t0, s, acc, sh.red);
   TRACE_POINT(3);
-  TRACE_HWID(7);
+  TRACE_HWID(15);
 }
 
 // MXFP4 tiles work in units of 4 K steps of 128 (512 K): one weight-scale dword and one
@@ -948,7 +948,7 @@ __device__ void proj_mx(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   TRACE_POINT(2);
   publish_tiles(a, t0, s, acc);
   TRACE_POINT(3);
-  TRACE_HWID(7);
+  TRACE_HWID(15);
 }
 
 // MXFP6 E2M3 in_proj_qkvz with bf16 activations (W6A16, "vLLM PR #60833", a reviewer's
@@ -1050,7 +1050,7 @@ __device__ void proj_mx6(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   TRACE_POINT(2);
   publish_tiles(a, t0, s, acc);
   TRACE_POINT(3);
-  TRACE_HWID(7);
+  TRACE_HWID(15);
 }
 
 // projection workgroup gb: groups of 4 in_proj_qkvz tiles first, then the b|a tiles; S K
@@ -1337,7 +1337,9 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
           sh.scal[2] = __expf(-__expf(alog) * sp);  // exp(g), g = -exp(A_log) softplus(a + dt_bias)
         }
       }
+      TRACE_POINT(8);
       __syncthreads();
+      TRACE_POINT(9);
       const int ty = MULTI ? t : 0;
       const int j = tid - 128;
       if (qk_thread) {
@@ -1376,14 +1378,17 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
         v[9] = fmaf(q, q, v[9]);
         v[10] = fmaf(k, q, v[10]);
       }
+      TRACE_POINT(10);
 #pragma unroll
       for (int mask = QW; mask < 64; mask <<= 1) {
 #pragma unroll
         for (int e = 0; e < 11; ++e) v[e] += __shfl_xor(v[e], mask, 64);
       }
       TRACE_POINT(6);
-      const float kscale = 1.0f / sqrtf(v[8] + a.l2eps);                                   // 1 / |k|
-      const float qscale = (1.0f / sqrtf(v[9] + a.l2eps)) * (1.0f / sqrtf((float)DK));   // 1 / (|q| sqrt(dk))
+      // reciprocal square roots on the hardware instruction (within 1 ulp)
+      constexpr float kInvSqrtDk = DK == 32 ? 0.17677669529663687f : DK == 64 ? 0.125f : 0.08838834764831845f;
+      const float kscale = __builtin_amdgcn_rsqf(v[8] + a.l2eps);                 // 1 / |k|
+      const float qscale = __builtin_amdgcn_rsqf(v[9] + a.l2eps) * kInvSqrtDk;    // 1 / (|q| sqrt(dk))
       const float decay = sh.scal[2], beta = sh.scal[3];
       const float kq = v[10] * kscale * qscale;  // (normalised k) . (normalised, scaled q)
       // With u = S^T k and w = S^T q of the old state, the updated state
@@ -1394,20 +1399,31 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
         d[c] = beta * (sh.vs[4 * cq + c] - decay * (v[c] * kscale));
         ob[c] = rbf(fmaf(d[c], kq, decay * (v[4 + c] * qscale)));
       }
-      // the state update and its stores go first; the gated norm needs a sum over all columns
+      TRACE_POINT(11);
+      // RMSNormGated over the head. Every row group of a wave holds the wave's DV / 4
+      // columns once: the sum of ob^2 over its QW column quads (an xor butterfly over the
+      // quad bits of the lane id, fixed order), then over the 4 waves through LDS.
+      float ss = (ob[0] * ob[0] + ob[1] * ob[1]) + (ob[2] * ob[2] + ob[3] * ob[3]);
 #pragma unroll
-      for (int m = 0; m < RPT; ++m) {
-        const float kh = sh.ks[rg + NRG * m] * kscale;
+      for (int mask = 1; mask < QW; mask <<= 1) ss += __shfl_xor(ss, mask, 64);
+      if (lane == 0) sh.bsum[tid >> 6] = ss;
+      // The state update and its stores overlap the exchange; with the out_proj fold they
+      // follow the core row instead, whose completion is signalled before they are issued.
+      auto update_state = [&]() {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) S[m][c] = fmaf(decay, S[m][c], kh * d[c]);
-        if (keep) StateIO<ST>::store(a.ssm, dslot * tile + hoff + (size_t)(rg + NRG * m) * DV, S[m]);
-      }
+        for (int m = 0; m < RPT; ++m) {
+          const float kh = sh.ks[rg + NRG * m] * kscale;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) S[m][c] = fmaf(decay, S[m][c], kh * d[c]);
+          if (keep) StateIO<ST>::store(a.ssm, dslot * tile + hoff + (size_t)(rg + NRG * m) * DV, S[m]);
+        }
+      };
+      if (!a.fold) update_state();
       TRACE_POINT(7);
-      // RMSNormGated over the head: the lanes of row group 0 hold each column once
-      float ss = 0.0f;
-      if (rg == 0) ss = (ob[0] * ob[0] + ob[1] * ob[1]) + (ob[2] * ob[2] + ob[3] * ob[3]);
-      ss = block_sum(ss, sh.bsum);
-      const float rstd = 1.0f / sqrtf(ss / (float)DV + a.geps);
+      __syncthreads();
+      ss = (sh.bsum[0] + sh.bsum[1]) + (sh.bsum[2] + sh.bsum[3]);
+      TRACE_POINT(12);
+      const float rstd = __builtin_amdgcn_rsqf(ss * (1.0f / (float)DV) + a.geps);
       if (rg == 0) {
         const float g0 = bf2f((uint16_t)gw4.x), g1 = bf2f((uint16_t)(gw4.x >> 16));
         const float g2 = bf2f((uint16_t)gw4.y), g3 = bf2f((uint16_t)(gw4.y >> 16));
@@ -1420,6 +1436,12 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
         else
           *dst = o;
       }
+      if (a.fold) {  // the head's core row is in place for the out_proj workgroups (one token)
+        wait_stores();
+        __syncthreads();
+        if (tid < kCoreCopies) add_agent(sy(a, kSyCoreDone + tid), 1u);
+        update_state();
+      }
       TRACE_POINT(3);
     }
     if (qk_owner && tid == 0 && a.r > 1) st_agent(sy(a, sy_conv(a, seq, kap)), 0u);
@@ -1431,7 +1453,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
       for (int j = 2 * tid; j < DV; j += 2 * kThreads) st_agent(reinterpret_cast<uint32_t*>(core + j), 0u);
     }
   }
-  if (a.fold) {  // the core rows of this head are in place for the out_proj workgroups
+  if (a.fold && !valid) {  // the pad row's zero core row is in place for the out_proj workgroups
     wait_stores();
     __syncthreads();
     if (tid < kCoreCopies) add_agent(sy(a, kSyCoreDone + tid), 1u);
