@@ -128,6 +128,65 @@ __device__ __forceinline__ float block_sum(float v, float* lds) {
   return r;
 }
 
+// Cross-lane exchanges on the VALU instead of the LDS crossbar. dpp<CTRL>(v): v from the
+// lane that the DPP control picks (row_ror:8 = 0x128, a rotation by 8 within each row of 16
+// lanes, is the xor-8 partner; quad_perm [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E the xor-1
+// and xor-2 partners; row_half_mirror = 0x141 pairs lane i with 7 - i within 8 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// v[e] += (v[e] in lane ^ M) for e < 4, M = 16 or 32, with gfx950's v_permlane16_swap /
+// v_permlane32_swap: swapping a copy of v with another copy leaves each lane's xor
+// partner in one of the two (rows 2j+1 with rows 2j of the other, or the upper half with
+// the lower half). Inline asm, padded with s_nop on both sides: a swap that reads a VGPR
+// the previous VALU instruction wrote reads its old value (measured on MI355X), and the
+// compiler does not insert wait states for inline asm.
+template <int M>
+__device__ __forceinline__ void xor_add4(float& v0, float& v1, float& v2, float& v3) {
+  float a0 = v0, b0 = v0, a1 = v1, b1 = v1, a2 = v2, b2 = v2, a3 = v3, b3 = v3;
+  if constexpr (M == 16)
+    asm volatile(
+        "s_nop 4\n\tv_permlane16_swap_b32 %0, %1\n\tv_permlane16_swap_b32 %2, %3\n\t"
+        "v_permlane16_swap_b32 %4, %5\n\tv_permlane16_swap_b32 %6, %7\n\ts_nop 4"
+        : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "+v"(a2), "+v"(b2), "+v"(a3), "+v"(b3));
+  else
+    asm volatile(
+        "s_nop 4\n\tv_permlane32_swap_b32 %0, %1\n\tv_permlane32_swap_b32 %2, %3\n\t"
+        "v_permlane32_swap_b32 %4, %5\n\tv_permlane32_swap_b32 %6, %7\n\ts_nop 4"
+        : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "+v"(a2), "+v"(b2), "+v"(a3), "+v"(b3));
+  // the partner is in a for the odd row (M = 16) or upper half (M = 32), else in b
+  const bool hi = (threadIdx.x & M) != 0;
+  v0 += hi ? a0 : b0;
+  v1 += hi ? a1 : b1;
+  v2 += hi ? a2 : b2;
+  v3 += hi ? a3 : b3;
+}
+// v[e] += (v[e] in lane ^ M) for every e, M a power of two below 64; each pair adds the
+// same two values (in either order), so both lanes hold the same sum
+template <int M, int N>
+__device__ __forceinline__ void xor_add(float (&v)[N]) {
+  if constexpr (M == 16 || M == 32) {
+#pragma unroll
+    for (int e = 0; e < N; e += 4) {
+      float d0 = 0.0f, d1 = 0.0f, d2 = 0.0f;
+      xor_add4<M>(v[e], e + 1 < N ? v[e + 1] : d0, e + 2 < N ? v[e + 2] : d1, e + 3 < N ? v[e + 3] : d2);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) v[e] += M == 8 ? dpp<0x128>(v[e]) : __shfl_xor(v[e], M, 64);
+  }
+}
+// the xor butterfly over lane bits M, 2M, ... 32: every lane ends with the sum over its
+// 64 / M lanes that agree with it on the bits below M
+template <int M, int N>
+__device__ __forceinline__ void xor_butterfly(float (&v)[N]) {
+  if constexpr (M < 64) {
+    xor_add<M>(v);
+    xor_butterfly<2 * M>(v);
+  }
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
@@ -1226,8 +1285,9 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   constexpr int DV = DK;
   // State tile layout: wave w owns the columns [w DV/4, (w+1) DV/4) as QW quads of 4
   // columns; its 64 lanes are QW quads x NRG row groups, lane = rg * QW + quad, and a lane
-  // holds rows rg + NRG m (m < RPT) of its 4 columns. Sums over the key dim (S^T k, S^T q)
-  // then stay inside a wave: an xor butterfly over the row-group bits of the lane id.
+  // holds rows rg RPT + m (m < RPT) of its 4 columns (contiguous, so its k and q values are
+  // a few 16-byte LDS reads). Sums over the key dim (S^T k, S^T q) then stay inside a wave:
+  // an xor butterfly over the row-group bits of the lane id.
   constexpr int QW = DV / 16;          // column quads per wave
   constexpr int NRG = 64 / QW;         // row groups per wave
   constexpr int RPT = DK / NRG;        // state rows per lane
@@ -1248,7 +1308,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   const bool qk_thread = tid < DK, v_thread = tid >= 128 && tid < 128 + DV;
   if (valid) {
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) StateIO<ST>::load(a.ssm, slot * tile + hoff + (size_t)(rg + NRG * m) * DV, S[m]);
+    for (int m = 0; m < RPT; ++m) StateIO<ST>::load(a.ssm, slot * tile + hoff + (size_t)(rg * RPT + m) * DV, S[m]);
     if (qk_thread) {
       conv_load(a, slot, kap * DK + tid, c0);
       conv_load(a, slot, a.nk * DK + kap * DK + tid, c1);
@@ -1367,7 +1427,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
       float v[11] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int m = 0; m < RPT; ++m) {
-        const int i = rg + NRG * m;
+        const int i = rg * RPT + m;
         const float k = sh.ks[i], q = sh.qs[i];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -1379,11 +1439,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
         v[10] = fmaf(k, q, v[10]);
       }
       TRACE_POINT(10);
-#pragma unroll
-      for (int mask = QW; mask < 64; mask <<= 1) {
-#pragma unroll
-        for (int e = 0; e < 11; ++e) v[e] += __shfl_xor(v[e], mask, 64);
-      }
+      xor_butterfly<QW>(v);
       TRACE_POINT(6);
       // reciprocal square roots on the hardware instruction (within 1 ulp)
       constexpr float kInvSqrtDk = DK == 32 ? 0.17677669529663687f : DK == 64 ? 0.125f : 0.08838834764831845f;
@@ -1404,18 +1460,19 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
       // columns once: the sum of ob^2 over its QW column quads (an xor butterfly over the
       // quad bits of the lane id, fixed order), then over the 4 waves through LDS.
       float ss = (ob[0] * ob[0] + ob[1] * ob[1]) + (ob[2] * ob[2] + ob[3] * ob[3]);
-#pragma unroll
-      for (int mask = 1; mask < QW; mask <<= 1) ss += __shfl_xor(ss, mask, 64);
+      if (QW >= 2) ss += dpp<0xB1>(ss);  // xor 1
+      if (QW >= 4) ss += dpp<0x4E>(ss);  // xor 2
+      if (QW >= 8) ss += dpp<0x141>(ss);  // the other quad of lanes among 8 (mirror)
       if (lane == 0) sh.bsum[tid >> 6] = ss;
       // The state update and its stores overlap the exchange; with the out_proj fold they
       // follow the core row instead, whose completion is signalled before they are issued.
       auto update_state = [&]() {
 #pragma unroll
         for (int m = 0; m < RPT; ++m) {
-          const float kh = sh.ks[rg + NRG * m] * kscale;
+          const float kh = sh.ks[rg * RPT + m] * kscale;
 #pragma unroll
           for (int c = 0; c < 4; ++c) S[m][c] = fmaf(decay, S[m][c], kh * d[c]);
-          if (keep) StateIO<ST>::store(a.ssm, dslot * tile + hoff + (size_t)(rg + NRG * m) * DV, S[m]);
+          if (keep) StateIO<ST>::store(a.ssm, dslot * tile + hoff + (size_t)(rg * RPT + m) * DV, S[m]);
         }
       };
       if (!a.fold) update_state();
