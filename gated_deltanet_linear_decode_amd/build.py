@@ -1,6 +1,9 @@
 """Compile the HIP library (libgdn_block.so) in-tree for gfx950.
 
-    python -m gated_deltanet_linear_decode_amd.build
+    python -m gated_deltanet_linear_decode_amd.build           # libgdn_block.so
+    python -m gated_deltanet_linear_decode_amd.build --trace   # libgdn_block_trace.so: the same
+        kernels with per-workgroup wall-clock stamps (GDN_TRACE), read by
+        python -m gated_deltanet_linear_decode_amd.timeline
 """
 from __future__ import annotations
 
@@ -12,6 +15,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgdn_block.so")
+TRACE_LIB = os.path.join(PKG, "libgdn_block_trace.so")
 SOURCES = [os.path.join(PKG, "csrc", "gdn_block.hip")]
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [
@@ -21,10 +25,13 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into the shared library; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+def build(verbose: bool = False, trace: bool = False) -> str:
+    """Compile every source into the shared library (with `trace`, the profiling build);
+    returns its path."""
+    lib = TRACE_LIB if trace else LIB
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(["-DGDN_TRACE"] if trace else []), "-I", os.path.join(ROOT, "include"), *SOURCES,
+           "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -33,9 +40,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
     if verbose and errs:
         print("\n".join(errs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, trace="--trace" in sys.argv[1:]))
