@@ -465,6 +465,38 @@ __device__ void norm_rstd_role(const Args& a, int row, float* red) {
   TRACE_POINT(3);
 }
 
+// MXFP4 image of one 2048-wide slice of a row (8 bf16 per thread): codes and the grouped
+// scale dwords, stored coherently for the projection workgroups
+__device__ __forceinline__ void store_image(const Args& a, int row, int mi, const u32x4_t& o4) {
+  const int H = a.H, tid = threadIdx.x;
+  // H is a multiple of 512, so a wave's 64 chunks are all in range together
+  uint32_t v[4] = {o4[0], o4[1], o4[2], o4[3]}, eb;
+  st_agent(a.xq + (size_t)row * (H >> 3) + mi, mx_quant8(v, eb, a.mx_ceil));
+  // The wave's 64 chunks are the 16 blocks of 4 K steps of 128: block 4 s + kb holds
+  // K quarter kb of step s. Scales are stored per (4 steps, quarter kb) as one dword,
+  // byte s, the operand a projection lane of quarter kb reads for 4 steps at once.
+  const int lane = tid & 63, kb = (lane >> 2) & 3;
+  uint32_t d = 0;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) d |= (uint32_t)__shfl((int)eb, 16 * st + 4 * kb, 64) << (8 * st);
+  if (lane < 16 && (lane & 3) == 0) st_agent(a.xqs + (size_t)row * (H >> 7) + 4 * (mi >> 6) + kb, d);
+}
+
+// With a normed input and MXFP4 at more than 4 rows: P workgroups per row quantise x (which
+// is xn) once, 2048 columns each, into the shared image, instead of every projection
+// workgroup quantising its K range of every row (measured faster past 4 rows).
+__device__ void quant_role(const Args& a, int b) {
+  const int row = b / a.P, part = b - row * a.P, mi = part * kThreads + threadIdx.x;
+  if (mi < (a.H >> 3)) {
+    const uint4 q = reinterpret_cast<const uint4*>(a.x + (size_t)row * a.H)[mi];
+    store_image(a, row, mi, u32x4_t{q.x, q.y, q.z, q.w});
+  }
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x < kNormCopies) add_agent(sy(a, kSyNorm + threadIdx.x), 1u);
+  if (threadIdx.x == 0) add_agent(sy(a, kSyNormExit), 1u);
+}
+
 template <bool MX>
 __device__ void norm_role(const Args& a, int b, float* red) {
   // P workgroups per row: each loads and sums the whole row (the same sum in the same
@@ -527,19 +559,7 @@ __device__ void norm_role(const Args& a, int b, float* red) {
       o4[k] = f2bf2(bf2f((uint16_t)ph[k]) * rstd * (1.0f + bf2f((uint16_t)pw[k])),
                     bf2f((uint16_t)(ph[k] >> 16)) * rstd * (1.0f + bf2f((uint16_t)(pw[k] >> 16))));
     st_agent16(reinterpret_cast<uint32_t*>(a.xn + (size_t)row * H) + 4 * mi, o4);
-    if (MX) {
-      // H is a multiple of 512, so a wave's 64 chunks are all in range together
-      uint32_t v[4] = {o4[0], o4[1], o4[2], o4[3]}, eb;
-      st_agent(a.xq + (size_t)row * (H >> 3) + mi, mx_quant8(v, eb, a.mx_ceil));
-      // The wave's 64 chunks are the 16 blocks of 4 K steps of 128: block 4 s + kb holds
-      // K quarter kb of step s. Scales are stored per (4 steps, quarter kb) as one dword,
-      // byte s, the operand a projection lane of quarter kb reads for 4 steps at once.
-      const int lane = tid & 63, kb = (lane >> 2) & 3;
-      uint32_t d = 0;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) d |= (uint32_t)__shfl((int)eb, 16 * st + 4 * kb, 64) << (8 * st);
-      if (lane < 16 && (lane & 3) == 0) st_agent(a.xqs + (size_t)row * (H >> 7) + 4 * (mi >> 6) + kb, d);
-    }
+    if (MX) store_image(a, row, mi, o4);
   }
   TRACE_POINT(2);
   wait_stores();
@@ -688,7 +708,8 @@ __device__ __forceinline__ void stage_xn(const Args& a, int gb, int k0, ProjShar
 // projection workgroup issues the loads of its K range of x before its weight loads, so
 // they return first, and stores them to LDS (bf16), or quantises them into the MXFP4 image
 // there ("SGLang PR #43558", Modifications: the normed build, every CTA quantising the
-// rows itself).
+// rows itself). MXFP4 past 4 rows instead reads the image the quantiser workgroups make
+// once per row: quantising every row in every workgroup costs more there than the wait.
 constexpr int kXnChunks = GDN_MAX_ROWS * kKr / 8 / kThreads;  // 16-byte chunks per thread at most
 struct XnIn {
   u32x4_t v[kXnChunks];
@@ -978,13 +999,14 @@ __device__ void proj_mx(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   const int rot = (t * 7 + s * 3) % nu;   // spread concurrent streams over the channels
   auto lunit = [&](int m) { return m + rot < nu ? m + rot : m + rot - nu; };
   XnIn xi;
-  if (a.normed) xqin_issue(a, s * a.Kr, xi);
+  const bool own = a.normed && a.P == 0;  // quantise the K range here (a normed input at <= 4 rows)
+  if (own) xqin_issue(a, s * a.Kr, xi);
   MxUnit w[kWinMx];
 #pragma unroll
   for (int m = 0; m < kWinMx; ++m)
     if (m < nu) mx_wload<PACKED>(a, t, u0 + lunit(m), lane, w[m]);
 
-  if (a.normed)
+  if (own)
     xqin_store(a, xi, sh);
   else
     stage_xq(a, gb, s * a.Kr, sh);
@@ -1121,7 +1143,7 @@ __device__ void proj_role(const Args& a, int gb, ProjShared& sh) {
   // weight loads back by ~0.3 us lets the norm rows' loads through first. Measured at the
   // TP8-rank shape: 0.35-0.5 us faster at 1-8 rows, 0.05-0.1 us slower at 12-16 rows; with
   // bf16 or MXFP6 weights any delay costs time (the stream is the critical path there).
-  if (FMT == kFmtMx4 && !a.normed && a.R <= 8) __builtin_amdgcn_s_sleep(10);
+  if (FMT == kFmtMx4 && a.P > 0 && a.R <= 8) __builtin_amdgcn_s_sleep(10);
   if (gb < a.Gq) {
     const int tg = gb / a.S, s = gb - tg * a.S;
     if (FMT == kFmtMx4)
@@ -1640,7 +1662,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
   TRACE_POINT(0);
   const int nn = a.R * a.P, nr = a.Rs * a.nv;
   if (b < nn) {
-    if (FMT == kFmtMx4)
+    if (FMT == kFmtMx4 && a.normed)
+      quant_role(a, b);
+    else if (FMT == kFmtMx4)
       norm_role<true>(a, b, sh.rec.bsum);
     else
       norm_rstd_role(a, b, sh.rec.bsum);
@@ -2186,7 +2210,9 @@ int decode_impl(gdn_block* b, const Scratch& sc, const void* x, void* residual, 
   a.normed = normed ? 1 : 0;
   // norm workgroups per row: the MXFP4 image is made by ceil(H / 2048) of them, 2048 columns
   // each; otherwise one publishes the row's rstd
-  a.P = normed ? 0 : b->fmt == kFmtMx4 ? (c.hidden / 8 + kThreads - 1) / kThreads : 1;
+  // (a normed input has none, except MXFP4 past 4 rows: quantiser workgroups, 2048 columns each)
+  const int p_mx = (c.hidden / 8 + kThreads - 1) / kThreads;
+  a.P = normed ? (b->fmt == kFmtMx4 && rows * tokens > 4 ? p_mx : 0) : b->fmt == kFmtMx4 ? p_mx : 1;
   a.T = b->t;
   a.Tq = b->tq;
   a.Tb = b->tb;

@@ -119,6 +119,13 @@ def test_tp8_rank_mxfp4_verify():
     verify_case(configs.TP8_RANK_MXFP4, 4, 2, 712, flips=(0.02, 0.15))
 
 
+@pytest.mark.parametrize("R,T", [(2, 2), (3, 4)])
+def test_tp8_rank_mxfp4_normed_verify(R, T):
+    """A normed input with MXFP4: at 4 token rows each projection workgroup quantises its
+    K range itself, past 4 the quantiser workgroups make the image once per row."""
+    verify_case(configs.TP8_RANK_MXFP4_NORMED, R, T, 716 + R)
+
+
 def test_tp8_rank_mxfp6_normed_verify():
     verify_case(configs.TP8_RANK_MXFP6.with_(name="mx6_normed", input_normed=True, has_residual=False), 2, 4, 713)
 
