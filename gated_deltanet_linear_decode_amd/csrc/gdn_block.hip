@@ -61,6 +61,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "gdn_block.h"
 
@@ -482,9 +483,9 @@ __device__ __forceinline__ void store_image(const Args& a, int row, int mi, cons
   if (lane < 16 && (lane & 3) == 0) st_agent(a.xqs + (size_t)row * (H >> 7) + 4 * (mi >> 6) + kb, d);
 }
 
-// With a normed input and MXFP4 at more than 4 rows: P workgroups per row quantise x (which
+// With a normed input and MXFP4 at more than 2 rows: P workgroups per row quantise x (which
 // is xn) once, 2048 columns each, into the shared image, instead of every projection
-// workgroup quantising its K range of every row (measured faster past 4 rows).
+// workgroup quantising its K range of every row (measured faster from 3 rows on).
 __device__ void quant_role(const Args& a, int b) {
   const int row = b / a.P, part = b - row * a.P, mi = part * kThreads + threadIdx.x;
   if (mi < (a.H >> 3)) {
@@ -708,7 +709,7 @@ __device__ __forceinline__ void stage_xn(const Args& a, int gb, int k0, ProjShar
 // projection workgroup issues the loads of its K range of x before its weight loads, so
 // they return first, and stores them to LDS (bf16), or quantises them into the MXFP4 image
 // there ("SGLang PR #43558", Modifications: the normed build, every CTA quantising the
-// rows itself). MXFP4 past 4 rows instead reads the image the quantiser workgroups make
+// rows itself). MXFP4 past 2 rows instead reads the image the quantiser workgroups make
 // once per row: quantising every row in every workgroup costs more there than the wait.
 constexpr int kXnChunks = GDN_MAX_ROWS * kKr / 8 / kThreads;  // 16-byte chunks per thread at most
 struct XnIn {
@@ -999,7 +1000,7 @@ __device__ void proj_mx(const Args& a, int gb, int t0, int s, ProjShared& sh) {
   const int rot = (t * 7 + s * 3) % nu;   // spread concurrent streams over the channels
   auto lunit = [&](int m) { return m + rot < nu ? m + rot : m + rot - nu; };
   XnIn xi;
-  const bool own = a.normed && a.P == 0;  // quantise the K range here (a normed input at <= 4 rows)
+  const bool own = a.normed && a.P == 0;  // quantise the K range here (a normed input at <= 2 rows)
   if (own) xqin_issue(a, s * a.Kr, xi);
   MxUnit w[kWinMx];
 #pragma unroll
@@ -1195,6 +1196,7 @@ struct RecShared {
   float y[GDN_MAX_ROWS][4][128];             // per token: projection outputs q, k, v, z of the head (bf16
                                              // values); a decode step uses token 0 only
   float gt[GDN_MAX_ROWS][2];                 // verify: per token beta and exp(g)
+  int dst[GDN_MAX_ROWS];                     // verify: per token the slot its state goes to
   float qs[128], ks[128], vs[128];           // conv outputs q, k, v (SiLU, bf16 values)
   float scal[4];                             // [2] exp(g), [3] beta
   float bsum[4];
@@ -1293,6 +1295,34 @@ __device__ __forceinline__ void conv_roll(ConvIn& c, float y) {
   c.prev[kConvW - 2] = f2bf(y);
 }
 
+// The last recurrence workgroup past its waits clears the counters for the next launch
+// (its third wave, which holds the exit ticket in lane 0): by then every projection tile
+// has been counted (each group and the b|a tiles had a waiter), so every projection
+// workgroup is past its norm (or rstd) wait, and no recurrence workgroup reads a counter
+// again (the q|k conv counter is cleared by its owner).
+__device__ __forceinline__ void rec_clear(const Args& a, uint32_t exit_ticket) {
+  const int tid = threadIdx.x;
+  if ((tid >> 6) == 2 && __shfl((int)exit_ticket, 0, 64) == a.Rs * a.nv - 1) {
+    const int l = tid & 63;
+    if (l == 0) {  // the norm workgroups may still be rewriting residual rows (past their last wait)
+      int it = 0;
+      while (ld_agent(sy(a, kSyNormExit)) < (uint32_t)(a.R * a.P) && ++it <= a.spin) __builtin_amdgcn_s_sleep(4);
+      if (it > a.spin) __hip_atomic_fetch_or(sy(a, kSyError), kErrNormWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (l < kNormCopies) {
+      st_agent(sy(a, kSyNorm + l), 0u);
+      st_agent(sy(a, kSyLoaded + l), 0u);
+      for (int r = 0; r < a.R; ++r) st_agent(sy(a, kSyRstd + l) + r, 0u);
+    }
+    for (int i = l; i < a.nk * kGroupCopies; i += 64) st_agent(sy(a, kSyGroup0 + i), 0u);
+    if (l == 0) {
+      st_agent(sy(a, kSyNormExit), 0u);
+      st_agent(sy(a, kSyBa), 0u);
+      st_agent(sy(a, kSyExit), 0u);
+    }
+  }
+}
+
 // One workgroup per (sequence, value head). A decode step is a sequence of one token
 // whose state goes back to its own slot; a verify step runs the sequence's Tk tokens one
 // after the other from its source slot, keeping the state in registers, and stores the
@@ -1301,8 +1331,10 @@ __device__ __forceinline__ void conv_roll(ConvIn& c, float y) {
 // "sgl-amd-mono PR #89", Modifications, and "vLLM PR #60833", Limitations: K1 keeps no
 // state per draft token, so a rejected draft could not roll back). MULTI instantiates the
 // token loop; without it the loop runs once and compiles to the single-token code (the
-// loop-carried state tile costs registers the decode launches should not pay for).
-template <int DK, typename ST, bool MULTI>
+// loop-carried state tile costs registers the decode launches should not pay for). DST: a
+// single-token verify step, whose state goes to its destination slot (decode instantiations
+// never read the destination array: measured, even an untaken read of it costs them time).
+template <int DK, typename ST, bool MULTI, bool DST = false>
 __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   constexpr int DV = DK;
   // State tile layout: wave w owns the columns [w DV/4, (w+1) DV/4) as QW quads of 4
@@ -1320,6 +1352,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
   const bool qk_owner = hh == a.r - 1;  // writes the key head's q|k conv state
   const int slot = a.idx[seq];
   const bool valid = slot > 0 && slot < a.slots;
+  const int slot1 = DST ? a.dst[seq] : slot;  // where a single token's state goes
   const int lane = tid & 63, rg = lane / QW, cq = (tid >> 6) * QW + lane % QW;
   const size_t tile = ((size_t)a.nv * DK) * DV;  // state elements per slot
   const size_t hoff = ((size_t)h * DK) * DV + 4 * cq;
@@ -1362,6 +1395,7 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
       return gbase + (blk == 0 ? j : blk == 1 ? DK + j : blk == 2 ? 2 * DK + hh * DV + j
                                                       : 2 * DK + a.r * DV + hh * DV + j);
     };
+    TRACE_POINT(13);
     if constexpr (MULTI) {
       // every token's projection outputs and gates first, 256 / DK tokens per pass, so the
       // token loop below reads them from LDS instead of waiting for a load per token
@@ -1385,14 +1419,18 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
           sh.gt[t][0] = __builtin_amdgcn_rcpf(1.0f + __expf(-yg));
         }
       }
+      // the destination slots too: a load inside the token loop would wait for every store
+      // of the tokens before it (a wave's memory counter returns in order)
+      if (tid >= 192 && tid < 192 + Tk) sh.dst[tid - 192] = a.dst[seq * Tk + tid - 192];
       if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
     }
+    TRACE_POINT(14);
 #pragma unroll 1
     for (int t = 0; t < Tk; ++t) {
       const int n = seq * Tk + t;  // the token's projection row
-      const int dslot = MULTI ? a.dst[n] : slot;
-      const bool keep = dslot > 0 && dslot < a.slots;  // store the state after this token
       if (MULTI || t > 0) __syncthreads();  // the previous token is done with the shared arrays
+      const int dslot = MULTI ? sh.dst[t] : slot1;
+      const bool keep = dslot > 0 && dslot < a.slots;  // store the state after this token
       if constexpr (MULTI) {
         if (tid == 0) {
           sh.scal[3] = sh.gt[t][0];
@@ -1538,31 +1576,403 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
     if (tid < kCoreCopies) add_agent(sy(a, kSyCoreDone + tid), 1u);
   }
 
-  // The last recurrence workgroup past its waits clears the counters for the next launch
-  // (its third wave, which holds the exit ticket in lane 0): by then every projection tile
-  // has been counted (each group and the b|a tiles had a waiter), so every projection
-  // workgroup is past its norm (or rstd) wait, and no recurrence workgroup reads a counter
-  // again (the q|k conv counter is cleared by its owner).
-  if ((tid >> 6) == 2 && __shfl((int)exit_ticket, 0, 64) == a.Rs * a.nv - 1) {
-    const int l = tid & 63;
-    if (l == 0) {  // the norm workgroups may still be rewriting residual rows (past their last wait)
-      int it = 0;
-      while (ld_agent(sy(a, kSyNormExit)) < (uint32_t)(a.R * a.P) && ++it <= a.spin) __builtin_amdgcn_s_sleep(4);
-      if (it > a.spin) __hip_atomic_fetch_or(sy(a, kSyError), kErrNormWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  rec_clear(a, exit_ticket);
+  TRACE_POINT(4);
+}
+
+// ---------------------------------------------------------------------------------------
+// role 3, verify steps of more than one token at head dim 128: the delta rule unrolled over
+// the step's tokens, so that only the elementwise state update stays serial. With k_t and
+// q_t normalised (q_t also scaled by 1/sqrt(dk)), a_t = exp(g_t), Gm(i..t) the product of
+// a_i .. a_t (1 when empty) and S0 the state the step starts from, substituting the update
+// S_t = a_t S_{t-1} + k_t d_t^T into itself gives
+//   a_t S_{t-1}^T k_t = Gm(0..t) S0^T k_t + sum_{j<t} Gm(j+1..t) (k_j . k_t) d_j
+//   d_t = beta_t (v_t - a_t S_{t-1}^T k_t)
+//   o_t = S_t^T q_t   = Gm(0..t) S0^T q_t + sum_{j<=t} Gm(j+1..t) (k_j . q_t) d_j
+// (the recurrence the decode steps run, one token after the other, in another order of
+// rounding). So: S0^T k_t and S0^T q_t for every token at once, and the key and query dot
+// products, are matrix-core products (bf16 operands: the conv outputs are bf16 values, and
+// so is a bf16 state; an f32 state goes in as two bf16 terms, hi + lo, which keeps about 16
+// significant bits of each element); the per-token scalars and the coefficients are small
+// tables in LDS; d_t and o_t follow per column, a forward substitution over the tokens;
+// then the gated norm and the core rows of all tokens; and last the serial part, the state
+// update and the snapshot stores, with no barrier and no wait between the tokens.
+struct VerShared {
+  float y[GDN_MAX_ROWS][4][128];  // per token: projections q, k, v, z; then q, k, v conv outputs
+  float u[GDN_MAX_ROWS][128];     // S0^T k_t (k not normalised), then d_t
+  float w[GDN_MAX_ROWS][128];     // S0^T q_t (q not normalised), then o_t (bf16 values)
+  float kk[GDN_MAX_ROWS][GDN_MAX_ROWS + 1];  // k_t . k_j, then Gm(j+1..t) (k_j . k_t), j < t
+  float qk[GDN_MAX_ROWS][GDN_MAX_ROWS + 1];  // q_t . k_j, then Gm(j+1..t) (k_j . q_t), j <= t
+  float qq[GDN_MAX_ROWS];                    // q_t . q_t
+  float ks[GDN_MAX_ROWS], qs[GDN_MAX_ROWS];  // 1 / |k_t|, 1 / (|q_t| sqrt(dk))
+  float gc[GDN_MAX_ROWS];                    // Gm(0..t)
+  float gt[GDN_MAX_ROWS][2];                 // beta_t, a_t
+  float ga[GDN_MAX_ROWS];                    // a_t again, contiguous
+  int dst[GDN_MAX_ROWS];                     // the slot the state after token t goes to
+};
+
+// bf16 pair of two floats that are bf16 values (exact: their low 16 bits are zero)
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  return (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xffff0000u);
+}
+// bf16 image of 8 consecutive floats in LDS that are bf16 values
+__device__ __forceinline__ u32x4_t bf16x8_of(const float* p) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p), b = *reinterpret_cast<const f32x4_t*>(p + 4);
+  return u32x4_t{bf16_pair(a[0], a[1]), bf16_pair(a[2], a[3]), bf16_pair(b[0], b[1]), bf16_pair(b[2], b[3])};
+}
+
+// (Its profiling-build timeline points are few on purpose: more of them made that build of
+// the role spill registers, which distorts the timeline.)
+template <typename ST>
+__device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
+  constexpr int D = 128;
+  constexpr bool kF32 = sizeof(ST) == 4;
+  // State tile layout: wave w holds the column half ch = w & 1 and the row half rh = w >> 1;
+  // lane l holds the 4 columns 64 ch + 4 (l & 15) .. + 3 of the 16 rows 64 rh + 16 (l >> 4)
+  // .. + 15. Rows m0 .. m0 + 7 of one column j are then lane l's part of a 16x16x32 bf16
+  // matrix-core B operand (K index 8 (l >> 4) + i <-> row 64 rh + 16 (l >> 4) + m0 + i,
+  // N index l & 15 <-> column 64 ch + 4 (l & 15) + j), and a store of row m covers 64
+  // contiguous columns of 4 rows, whole 128-byte lines.
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int ch = wave & 1, rh = wave >> 1, qd = lane & 15, rg = lane >> 4;
+  const int r0 = 64 * rh + 16 * rg, c0 = 64 * ch + 4 * qd;
+  const int seq = rb / a.nv, h = rb - seq * a.nv, Tk = a.Tk;
+  const int kap = h / a.r, hh = h - kap * a.r;
+  const bool qk_owner = hh == a.r - 1;
+  const int slot = a.idx[seq];
+  const bool valid = slot > 0 && slot < a.slots;
+  const size_t tile = ((size_t)a.nv * D) * D;
+  const size_t hoff = ((size_t)h * D) * D + c0;
+
+  // The old state: an f32 pool's rows as f32; a bf16 pool's rows kept as loaded (2 bf16
+  // pairs per row, half the registers) until the serial part needs them as f32.
+  float S[16][4];
+  uint32_t Sb[16][2];
+  ConvIn c0c, c1c;  // threads < 128: q and k channel tid; threads 128..255: v channel tid - 128
+  const bool qk_thread = tid < D;
+  if (valid) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const size_t off = slot * tile + hoff + (size_t)(r0 + m) * D;
+      if constexpr (kF32) {
+        StateIO<float>::load(a.ssm, off, S[m]);
+      } else {
+        const uint2 q = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.ssm) + off);
+        Sb[m][0] = q.x, Sb[m][1] = q.y;
+      }
     }
-    if (l < kNormCopies) {
-      st_agent(sy(a, kSyNorm + l), 0u);
-      st_agent(sy(a, kSyLoaded + l), 0u);
-      for (int r = 0; r < a.R; ++r) st_agent(sy(a, kSyRstd + l) + r, 0u);
-    }
-    for (int i = l; i < a.nk * kGroupCopies; i += 64) st_agent(sy(a, kSyGroup0 + i), 0u);
-    if (l == 0) {
-      st_agent(sy(a, kSyNormExit), 0u);
-      st_agent(sy(a, kSyBa), 0u);
-      st_agent(sy(a, kSyExit), 0u);
+    if (qk_thread) {
+      conv_load(a, slot, kap * D + tid, c0c);
+      conv_load(a, slot, a.nk * D + kap * D + tid, c1c);
+    } else {
+      conv_load(a, slot, 2 * a.nk * D + h * D + (tid - D), c0c);
     }
   }
-  TRACE_POINT(4);
+  const float alog = a.A_log[h], dtb = bf2f(a.dt_bias[h]);
+  const int p16 = tid & 15;  // the 8 columns 8 p16 .. + 7 of the output phase
+  const uint4 gw8 = *reinterpret_cast<const uint4*>(a.gnw + 8 * p16);
+  if (valid && !qk_owner) {
+    // the old q|k conv rows are in registers: let the owner overwrite them
+    wait_stores();
+    __syncthreads();
+    if (tid == 0) add_agent(sy(a, sy_conv(a, seq, kap)), 1u);
+  }
+  wait_group(a, kap);
+  wait_count(sy(a, kSyBa), (uint32_t)(a.Tb * a.S), sy(a, kSyError), kErrGroupWait, a.spin);
+  TRACE_POINT(1);
+
+  uint32_t exit_ticket = 0;
+  if (!valid) {
+    if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
+    for (int t = 0; t < Tk; ++t) {  // pad sequence: a zero core row for each of its tokens
+      uint16_t* core = a.core + (size_t)(seq * Tk + t) * a.nv * D + (size_t)h * D;
+      if (tid < D / 2) st_agent(reinterpret_cast<uint32_t*>(core) + tid, 0u);
+    }
+    rec_clear(a, exit_ticket);
+    return;
+  }
+  if (qk_owner && a.r > 1)  // the key head's other value heads have read the old q|k conv rows
+    wait_count(sy(a, sy_conv(a, seq, kap)), (uint32_t)(a.r - 1), sy(a, kSyError), kErrConvWait, a.spin);
+
+  // every token's projection outputs (q | k | v | z quads of the head), 2 tokens per pass
+  // and kVerPasses passes' loads in flight together (each pass holds S 16-byte loads while
+  // the state tile is in registers too); the gates and the destination slots
+  {
+    constexpr int kVerPasses = 2;
+    const int gbase = kap * a.GW, q = tid & 127, blk = q >> 5, j = 4 * (q & 31);
+    const int chn = gbase + (blk == 0 ? j : blk == 1 ? D + j : blk == 2 ? 2 * D + hh * D + j
+                                                      : 2 * D + a.r * D + hh * D + j);
+#pragma unroll 1
+    for (int p0 = 0; p0 < Tk; p0 += 2 * kVerPasses) {
+      f32x4_t v[kVerPasses];
+#pragma unroll
+      for (int u = 0; u < kVerPasses; ++u)
+        v[u] = proj_quad(a, seq * Tk + min(p0 + 2 * u + (tid >> 7), Tk - 1), chn);
+#pragma unroll
+      for (int u = 0; u < kVerPasses; ++u) {
+        const int t = p0 + 2 * u + (tid >> 7);
+        if (t < Tk) *reinterpret_cast<f32x4_t*>(&sh.y[t][blk][j]) = v[u];
+      }
+    }
+    if (tid < 2 * Tk) {  // even threads beta, odd threads a_t of token tid / 2
+      const int t = tid >> 1;
+      const float yg = proj_one(a, seq * Tk + t, a.Nq + kap * 2 * a.r + ((tid & 1) ? a.r : 0) + hh);
+      if (tid & 1) {
+        const float x = yg + dtb;
+        const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
+        sh.gt[t][1] = sh.ga[t] = __expf(-__expf(alog) * sp);  // exp(g), g = -exp(A_log) softplus(a + dt_bias)
+      } else {
+        sh.gt[t][0] = __builtin_amdgcn_rcpf(1.0f + __expf(-yg));  // beta = sigmoid(b)
+      }
+    }
+    if (tid >= 192 && tid < 192 + Tk) sh.dst[tid - 192] = a.dst[seq * Tk + tid - 192];
+    if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
+  }
+  __syncthreads();
+  TRACE_POINT(14);
+
+  // conv of every token, one channel per thread, in token order (measured faster than
+  // reading all of the channel's inputs first); the window after each kept token goes to
+  // its slot
+  if (qk_thread) {
+#pragma unroll 1
+    for (int t = 0; t < Tk; ++t) {
+      const float yq = sh.y[t][0][tid], yk = sh.y[t][1][tid];
+      sh.y[t][0][tid] = conv_out(c0c, yq);
+      sh.y[t][1][tid] = conv_out(c1c, yk);
+      const int ds = sh.dst[t];
+      if (qk_owner && ds > 0 && ds < a.slots) {
+        conv_store(a, ds, c0c, yq);
+        conv_store(a, ds, c1c, yk);
+      }
+      conv_roll(c0c, yq);
+      conv_roll(c1c, yk);
+    }
+  } else {
+    const int j = tid - D;
+#pragma unroll 1
+    for (int t = 0; t < Tk; ++t) {
+      const float yv = sh.y[t][2][j];
+      sh.y[t][2][j] = conv_out(c0c, yv);
+      const int ds = sh.dst[t];
+      if (ds > 0 && ds < a.slots) conv_store(a, ds, c0c, yv);
+      conv_roll(c0c, yv);
+    }
+  }
+  __syncthreads();
+  TRACE_POINT(2);
+
+  // S0^T k_t, then S0^T q_t, over this wave's 64 rows for all tokens: A operand = token
+  // (lane & 15)'s k (or q) at the same 8 rows as the B operand's K index. Lane l's result
+  // holds, for token 4 (l >> 4) + i, the columns c0 .. c0 + 3 (one per j): the upper row
+  // half's waves store theirs, then the lower half's add theirs to them.
+  const int ta = lane & 15;
+  const bool tok = ta < Tk;
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr) {  // pr 0: k (y block 1, into u); pr 1: q (block 0, into w)
+    f32x4_t acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m0 = 0; m0 < 16; m0 += 8) {
+      const u32x4_t av = tok ? bf16x8_of(&sh.y[ta][1 - pr][r0 + m0]) : zero;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // column j, rows m0 .. m0 + 7: a bf16 pool's halves as they are; an f32 element as
+        // hi + lo, both bf16 values
+        auto hi = [&](int i) { return rbf(S[m0 + i][j]); };
+        auto lo = [&](int i) { return rbf(S[m0 + i][j] - rbf(S[m0 + i][j])); };
+        auto col2 = [&](int i) {  // rows m0 + i, m0 + i + 1 of column j of a bf16 pool
+          const uint32_t x = Sb[m0 + i][j >> 1], y = Sb[m0 + i + 1][j >> 1];
+          return (j & 1) ? (x >> 16) | (y & 0xffff0000u) : (x & 0xffffu) | (y << 16);
+        };
+        u32x4_t bh;
+        if constexpr (kF32)
+          bh = u32x4_t{bf16_pair(hi(0), hi(1)), bf16_pair(hi(2), hi(3)), bf16_pair(hi(4), hi(5)),
+                       bf16_pair(hi(6), hi(7))};
+        else
+          bh = u32x4_t{col2(0), col2(2), col2(4), col2(6)};
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bh), acc[j], 0, 0, 0);
+        if constexpr (kF32) {
+          const u32x4_t bl = {bf16_pair(lo(0), lo(1)), bf16_pair(lo(2), lo(3)), bf16_pair(lo(4), lo(5)),
+                              bf16_pair(lo(6), lo(7))};
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bl), acc[j], 0, 0, 0);
+        }
+      }
+    }
+    float(*dst)[128] = pr == 0 ? sh.u : sh.w;
+    if (rh == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4_t*>(&dst[4 * rg + i][c0]) = f32x4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4_t* pd = reinterpret_cast<f32x4_t*>(&dst[4 * rg + i][c0]);
+        *pd = *pd + f32x4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+      }
+    }
+  }
+  // the tokens' dot products, one product per wave: k.k, q.k, q.q (16x16, tokens past Tk zero)
+  if (wave < 3) {
+    const int xa = wave == 0 ? 1 : 0, xb = wave == 2 ? 0 : 1;  // blocks: q 0, k 1
+    f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s4 = 0; s4 < D / 32; ++s4) {
+      const int k0 = 32 * s4 + 8 * rg;
+      const u32x4_t va = tok ? bf16x8_of(&sh.y[ta][xa][k0]) : zero;
+      const u32x4_t vb = tok ? bf16x8_of(&sh.y[ta][xb][k0]) : zero;
+      g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(vb), g, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // g[i] = row 4 (l >> 4) + i (the A token), column l & 15
+      const int m = 4 * rg + i, n = ta;
+      if (m < Tk && n < Tk) {
+        if (wave == 0) sh.kk[m][n] = g[i];
+        else if (wave == 1) sh.qk[m][n] = g[i];
+        else if (m == n) sh.qq[m] = g[i];
+      }
+    }
+  }
+  __syncthreads();
+  {  // the coefficient tables, one (t, j) per thread
+    const int t = tid >> 4, j = tid & 15;
+    if (t < Tk && j < Tk) {
+      // reciprocal square roots on the hardware instruction (within 1 ulp)
+      const float kt = __builtin_amdgcn_rsqf(sh.kk[t][t] + a.l2eps), kj = __builtin_amdgcn_rsqf(sh.kk[j][j] + a.l2eps);
+      const float qt = __builtin_amdgcn_rsqf(sh.qq[t] + a.l2eps) * 0.08838834764831845f;
+      float av4[GDN_MAX_ROWS];  // the decays, read together (no LDS round trip per factor)
+#pragma unroll
+      for (int i4 = 0; i4 < GDN_MAX_ROWS / 4; ++i4) {
+        const f32x4_t g4 = *reinterpret_cast<const f32x4_t*>(&sh.ga[4 * i4]);
+        av4[4 * i4] = g4[0], av4[4 * i4 + 1] = g4[1], av4[4 * i4 + 2] = g4[2], av4[4 * i4 + 3] = g4[3];
+      }
+      float gm = 1.0f;
+#pragma unroll
+      for (int i = 1; i < GDN_MAX_ROWS; ++i)
+        if (i > j && i <= t) gm *= av4[i];
+      // in place: each thread rewrites its own entry only, and the diagonal of kk, which
+      // the other threads read, stays (the coefficients of d_j in d_t need j < t only)
+      if (j < t) sh.kk[t][j] = gm * sh.kk[t][j] * kt * kj;
+      sh.qk[t][j] = j <= t ? gm * sh.qk[t][j] * qt * kj : 0.0f;
+      if (j == 0) {
+        sh.gc[t] = av4[0] * gm;
+        sh.ks[t] = kt;
+        sh.qs[t] = qt;
+      }
+    }
+  }
+  __syncthreads();
+
+  // d_t and o_t, one column per thread: a forward substitution over the tokens
+  if (tid < D) {
+    const int c = tid;
+    float dr[GDN_MAX_ROWS];
+#pragma unroll
+    for (int t = 0; t < GDN_MAX_ROWS; ++t) {
+      if (t < Tk) {
+        float acc = sh.gc[t] * (sh.u[t][c] * sh.ks[t]);
+#pragma unroll
+        for (int j = 0; j < t; ++j) acc = fmaf(sh.kk[t][j], dr[j], acc);
+        dr[t] = sh.gt[t][0] * (sh.y[t][2][c] - acc);
+        float o = sh.gc[t] * (sh.w[t][c] * sh.qs[t]);
+#pragma unroll
+        for (int j = 0; j <= t; ++j) o = fmaf(sh.qk[t][j], dr[j], o);
+        sh.u[t][c] = dr[t];
+        sh.w[t][c] = rbf(o);
+      }
+    }
+  }
+  __syncthreads();
+  TRACE_POINT(11);
+
+  // RMSNormGated and the core row of every token: 16 threads per token, 8 columns each
+  {
+    const int t = tid >> 4;
+    if (t < Tk) {
+      const f32x4_t o0 = *reinterpret_cast<const f32x4_t*>(&sh.w[t][8 * p16]);
+      const f32x4_t o1 = *reinterpret_cast<const f32x4_t*>(&sh.w[t][8 * p16 + 4]);
+      float ss = ((o0[0] * o0[0] + o0[1] * o0[1]) + (o0[2] * o0[2] + o0[3] * o0[3])) +
+                 ((o1[0] * o1[0] + o1[1] * o1[1]) + (o1[2] * o1[2] + o1[3] * o1[3]));
+      ss += dpp<0xB1>(ss);   // xor 1
+      ss += dpp<0x4E>(ss);   // xor 2
+      ss += dpp<0x141>(ss);  // the other quad among 8 (mirror)
+      ss += dpp<0x128>(ss);  // the other 8 among 16 (rotate by 8)
+      const float rstd = __builtin_amdgcn_rsqf(ss * (1.0f / (float)D) + a.geps);
+      const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(&sh.y[t][3][8 * p16]);
+      const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(&sh.y[t][3][8 * p16 + 4]);
+      auto gated = [&](float o, float z, uint32_t g, int hi) {
+        return o * rstd * bf2f((uint16_t)(hi ? g >> 16 : g)) * silu(z);
+      };
+      *reinterpret_cast<uint4*>(a.core + (size_t)(seq * Tk + t) * a.nv * D + (size_t)h * D + 8 * p16) =
+          make_uint4(f2bf2(gated(o0[0], z0[0], gw8.x, 0), gated(o0[1], z0[1], gw8.x, 1)),
+                     f2bf2(gated(o0[2], z0[2], gw8.y, 0), gated(o0[3], z0[3], gw8.y, 1)),
+                     f2bf2(gated(o1[0], z1[0], gw8.z, 0), gated(o1[1], z1[1], gw8.z, 1)),
+                     f2bf2(gated(o1[2], z1[2], gw8.w, 0), gated(o1[3], z1[3], gw8.w, 1)));
+    }
+  }
+  TRACE_POINT(12);
+
+  // the serial part: S_t = a_t S_{t-1} + k_t d_t^T, stored when the token's slot is valid
+  if constexpr (!kF32) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      S[m][0] = __builtin_bit_cast(float, Sb[m][0] << 16), S[m][1] = __builtin_bit_cast(float, Sb[m][0] & 0xffff0000u);
+      S[m][2] = __builtin_bit_cast(float, Sb[m][1] << 16), S[m][3] = __builtin_bit_cast(float, Sb[m][1] & 0xffff0000u);
+    }
+  }
+  // A token's LDS operands (its 16 key values of this lane's rows, d_t of its 4 columns,
+  // a_t, 1/|k_t|, the slot) are read together, one token ahead, so the loop waits on no
+  // LDS round trip; whether the snapshot is kept is one branch per token. (Measured: 8-byte
+  // row stores beat 16-byte stores that need the neighbour lanes to swap halves.)
+  struct TokIn {
+    f32x4_t k[4], d;
+    float dec, kst;
+    int ds;
+  };
+  auto tok_load = [&](int t, TokIn& v) {
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4) v.k[m4] = *reinterpret_cast<const f32x4_t*>(&sh.y[t][1][r0 + 4 * m4]);
+    v.d = *reinterpret_cast<const f32x4_t*>(&sh.u[t][c0]);
+    v.dec = sh.gt[t][1];
+    v.kst = sh.ks[t];
+    v.ds = sh.dst[t];
+  };
+  auto update = [&](const TokIn& v) {
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const float kh = v.k[m >> 2][m & 3] * v.kst;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) S[m][j] = fmaf(v.dec, S[m][j], kh * v.d[j]);
+    }
+  };
+  auto snapshot = [&](int ds) {
+    if (ds > 0 && ds < a.slots) {
+      const size_t base = ds * tile + hoff;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) StateIO<ST>::store(a.ssm, base + (size_t)(r0 + m) * D, S[m]);
+    }
+  };
+  // two operand sets in turn: token t + 1's are read while token t is computed
+  TokIn ta_, tb_;
+  tok_load(0, ta_);
+#pragma unroll 1
+  for (int t = 0; t < Tk; t += 2) {
+    if (t + 1 < Tk) tok_load(t + 1, tb_);
+    update(ta_);
+    snapshot(ta_.ds);
+    if (t + 1 < Tk) {
+      if (t + 2 < Tk) tok_load(t + 2, ta_);
+      update(tb_);
+      snapshot(tb_.ds);
+    }
+  }
+  TRACE_POINT(3);
+  if (qk_owner && tid == 0 && a.r > 1) st_agent(sy(a, sy_conv(a, seq, kap)), 0u);
+  rec_clear(a, exit_ticket);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1652,11 +2062,14 @@ __device__ void oproj_role(const Args& a, int ob, ProjShared& sh) {
 
 // FOLD is a template flag, not only a launch argument, so that the out_proj role's register
 // tile does not raise the register count (and lower the occupancy) of the launches without it.
-template <bool PACKED, int FMT, int DK, typename ST, bool FOLD, bool MULTI>
+template <bool PACKED, int FMT, int DK, typename ST, bool FOLD, bool MULTI, bool DST = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
+  // verify steps of more than one token at head dim 128 take the chunked recurrence and its
+  // larger shared arrays
+  constexpr bool kChunked = MULTI && DK == 128;
   __shared__ union {
     ProjShared proj;
-    RecShared rec;
+    std::conditional_t<kChunked, VerShared, RecShared> rec;
   } sh;
   const int b = blockIdx.x;
   TRACE_POINT(0);
@@ -1665,13 +2078,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
     if (FMT == kFmtMx4 && a.normed)
       quant_role(a, b);
     else if (FMT == kFmtMx4)
-      norm_role<true>(a, b, sh.rec.bsum);
+      norm_role<true>(a, b, &sh.proj.red[0][0]);
     else
-      norm_rstd_role(a, b, sh.rec.bsum);
+      norm_rstd_role(a, b, &sh.proj.red[0][0]);
   } else if (b < nn + a.G) {
     proj_role<PACKED, FMT>(a, b - nn, sh.proj);
   } else if (b < nn + a.G + nr) {
-    rec_role<DK, ST, MULTI>(a, b - nn - a.G, sh.rec);
+    if constexpr (kChunked)
+      rec_verify<ST>(a, b - nn - a.G, sh.rec);
+    else
+      rec_role<DK, ST, MULTI, DST>(a, b - nn - a.G, sh.rec);
   } else if (FOLD) {
     oproj_role<PACKED>(a, b - nn - a.G - nr, sh.proj);
   }
@@ -1946,6 +2362,9 @@ template <bool PACKED, int FMT, int DK, typename ST>
 void launch_st(const gdn_block* b, const Args& a, int grid, hipStream_t st) {
   if (b->fold)
     hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, true, false>), dim3(grid), dim3(kThreads), 0, st, a);
+  else if (DK == 128 && a.dst && a.Tk == 1)  // one token: the decode recurrence with its destination
+    hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, false, false, DK == 128>), dim3(grid), dim3(kThreads), 0,
+                       st, a);
   else if (a.dst)
     hipLaunchKernelGGL((decode_kernel<PACKED, FMT, DK, ST, false, true>), dim3(grid), dim3(kThreads), 0, st, a);
   else
@@ -2210,9 +2629,9 @@ int decode_impl(gdn_block* b, const Scratch& sc, const void* x, void* residual, 
   a.normed = normed ? 1 : 0;
   // norm workgroups per row: the MXFP4 image is made by ceil(H / 2048) of them, 2048 columns
   // each; otherwise one publishes the row's rstd
-  // (a normed input has none, except MXFP4 past 4 rows: quantiser workgroups, 2048 columns each)
+  // (a normed input has none, except MXFP4 past 2 rows: quantiser workgroups, 2048 columns each)
   const int p_mx = (c.hidden / 8 + kThreads - 1) / kThreads;
-  a.P = normed ? (b->fmt == kFmtMx4 && rows * tokens > 4 ? p_mx : 0) : b->fmt == kFmtMx4 ? p_mx : 1;
+  a.P = normed ? (b->fmt == kFmtMx4 && rows * tokens > 2 ? p_mx : 0) : b->fmt == kFmtMx4 ? p_mx : 1;
   a.T = b->t;
   a.Tq = b->tq;
   a.Tb = b->tb;

@@ -213,8 +213,11 @@ int gdn_block_decode_with_out_proj(gdn_block_t blk, const void* x, void* residua
 /* One launch over `rows` sequences of `tokens` tokens each (a speculative-decoding verify
  * step: the accepted token and its drafts), rows * tokens <= max_rows. Token t of sequence r
  * is row r * tokens + t of x, residual and core_out ([rows * tokens, ...], as in decode).
- * Each sequence starts from the state in slot src_idx[r] (device, [rows] int32) and runs
- * its tokens one after the other, as that many decode steps would; after token t the SSM
+ * Each sequence starts from the state in slot src_idx[r] (device, [rows] int32) and goes
+ * through its tokens in order, with the results that many decode steps would give (at
+ * head dim 128 and tokens > 1 in the chunked form: the recurrence unrolled over the step's
+ * tokens, the same arithmetic in another rounding order, so equal within rounding, not bit
+ * for bit; below 128 one token after the other); after token t the SSM
  * state and the conv window are stored into slot dst_idx[r * tokens + t] (device,
  * [rows, tokens] int32, 16-byte aligned), unless that index is <= 0 or >= num_state_slots
  * (then that snapshot is not kept). The source slot is only read, unless it is also one of

@@ -171,11 +171,11 @@ def test_exact_activations_tp8_rank_ceil_rule():
     _exact_case(configs.TP8_RANK_MXFP4.with_(name="tp8_rank_mxfp4_ceil", mx_scale_rule="ceil"), 8, 78)
 
 
-@pytest.mark.parametrize("rows", [1, 4, 5, 6, 16])
+@pytest.mark.parametrize("rows", [1, 2, 3, 6, 16])
 def test_tp8_rank_mxfp4_normed_input(rows):
     """With a normed input both sides quantise the same bf16 x, so no code can flip: the
-    strict element rule applies. Up to 4 rows every projection workgroup quantises its K
-    range of x itself; past 4 the quantiser workgroups make the shared image."""
+    strict element rule applies. Up to 2 rows every projection workgroup quantises its K
+    range of x itself; past 2 the quantiser workgroups make the shared image."""
     parity_case(configs.TP8_RANK_MXFP4_NORMED, rows, 51, dev=DEV)
 
 

@@ -7,9 +7,11 @@ draft is accepted (the follow-up "sgl-amd-mono PR #89", Modifications, and "vLLM
   snapshot (conv window and SSM state) by the parity rule, every other slot bitwise
   unchanged, pad sequences' core rows +0; row-major and tiled weights bit for bit.
 * GPU against GPU: one token with destination = source is gdn_block_decode bit for bit;
-  with an f32 pool, T tokens in one step end where T decode steps end, bit for bit (the
-  f32 state round-trips exactly, and projections are batch invariant); a sequence's
-  results do not depend on the other sequences of the step.
+  with an f32 pool, T tokens in one step end where T decode steps end, bit for bit where
+  the step runs its tokens one after the other (head dim below 128: the f32 state
+  round-trips exactly, and projections are batch invariant) and within the parity rule in
+  the chunked form (head dim 128); a sequence's results do not depend on the other
+  sequences of the step.
 """
 import numpy as np
 import pytest
@@ -119,10 +121,10 @@ def test_tp8_rank_mxfp4_verify():
     verify_case(configs.TP8_RANK_MXFP4, 4, 2, 712, flips=(0.02, 0.15))
 
 
-@pytest.mark.parametrize("R,T", [(2, 2), (3, 4)])
+@pytest.mark.parametrize("R,T", [(1, 2), (3, 4)])
 def test_tp8_rank_mxfp4_normed_verify(R, T):
-    """A normed input with MXFP4: at 4 token rows each projection workgroup quantises its
-    K range itself, past 4 the quantiser workgroups make the image once per row."""
+    """A normed input with MXFP4: at 2 token rows each projection workgroup quantises its
+    K range itself, past 2 the quantiser workgroups make the image once per row."""
     verify_case(configs.TP8_RANK_MXFP4_NORMED, R, T, 716 + R)
 
 
@@ -163,8 +165,14 @@ def test_one_token_verify_is_decode():
     _same(ver, dict(core=core.cpu(), residual=res.cpu(), conv_state=conv.cpu(), ssm_state=ssm.cpu()))
 
 
-def test_verify_equals_decode_chain_with_f32_state():
-    shape = configs.TP8_RANK_F32
+@pytest.mark.parametrize("name", ["tiny", "tp8_rank_f32"])
+def test_verify_equals_decode_chain_with_f32_state(name):
+    """With an f32 pool, T tokens of one verify step end where T decode steps end: bit for
+    bit where the verify step runs its tokens one after the other (head dim below 128),
+    within the parity rule at head dim 128, where it takes the chunked form (the same
+    arithmetic in another rounding order). The conv windows are copies: bit for bit."""
+    shape = TINY_V if name == "tiny" else configs.TP8_RANK_F32
+    exact = shape.head_k_dim < 128
     R, T = 3, 4
     w, c = synth.make_weights(shape, 721), synth.make_call(shape, R * T, 721)
     src, dst = verify_indices(shape, R, T, 721, pad=False, skip=False, in_place=False)
@@ -179,7 +187,10 @@ def test_verify_equals_decode_chain_with_f32_state():
         core = _decode(blk, shape, wd, cd.x[rows].contiguous(), res, conv, ssm, slots)
         torch.cuda.synchronize()
         got = u16(ver["core"])[rows.cpu().numpy()]
-        assert np.array_equal(u16(core), got), f"token {t}: core differs"
+        if exact:
+            assert np.array_equal(u16(core), got), f"token {t}: core differs"
+        else:
+            close(f"{name} chain token {t} core", got, u16(core))
         nxt = torch.from_numpy(dst[:, t].copy()).to(DEV)
         conv[nxt.long()] = conv[slots.long()]
         ssm[nxt.long()] = ssm[slots.long()]
@@ -188,7 +199,10 @@ def test_verify_equals_decode_chain_with_f32_state():
     # each decode step ran in place on the previous snapshot's slot, so only the last
     # snapshot survives in the chain's pools
     d = torch.from_numpy(dst[:, T - 1].astype(np.int64))
-    assert torch.equal(ver["ssm_state"][d], ssm.cpu()[d]), "final snapshot differs"
+    if exact:
+        assert torch.equal(ver["ssm_state"][d], ssm.cpu()[d]), "final snapshot differs"
+    else:
+        close(f"{name} chain final ssm", oracle_state(ver["ssm_state"][d]), oracle_state(ssm.cpu()[d]), bf16=False)
     assert torch.equal(ver["conv_state"][d].view(torch.int16), conv.cpu()[d].view(torch.int16))
 
 
