@@ -1597,10 +1597,20 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
 // tables in LDS; d_t and o_t follow per column, a forward substitution over the tokens;
 // then the gated norm and the core rows of all tokens; and last the serial part, the state
 // update and the snapshot stores, with no barrier and no wait between the tokens.
+// one token's rows, padded so that consecutive tokens start 16 bytes apart in the LDS
+// banks (lanes reading 16 tokens' rows at one offset, as the matrix-core operands do,
+// would otherwise all hit the same banks)
+struct TokRows {
+  float b[4][128];  // q, k, v, z
+  float pad[4];
+};
+constexpr int kURow = 132;  // padded row of u and w, for the same reason
+// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15)
+constexpr int kWaitVm0 = 0x0F70;
 struct VerShared {
-  float y[GDN_MAX_ROWS][4][128];  // per token: projections q, k, v, z; then q, k, v conv outputs
-  float u[GDN_MAX_ROWS][128];     // S0^T k_t (k not normalised), then d_t
-  float w[GDN_MAX_ROWS][128];     // S0^T q_t (q not normalised), then o_t (bf16 values)
+  TokRows y[GDN_MAX_ROWS];        // per token: projections q, k, v, z; then q, k, v conv outputs
+  float u[GDN_MAX_ROWS][kURow];   // S0^T k_t (k not normalised), then d_t
+  float w[GDN_MAX_ROWS][kURow];   // S0^T q_t (q not normalised), then o_t (bf16 values)
   float kk[GDN_MAX_ROWS][GDN_MAX_ROWS + 1];  // k_t . k_j, then Gm(j+1..t) (k_j . k_t), j < t
   float qk[GDN_MAX_ROWS][GDN_MAX_ROWS + 1];  // q_t . k_j, then Gm(j+1..t) (k_j . q_t), j <= t
   float qq[GDN_MAX_ROWS];                    // q_t . q_t
@@ -1702,6 +1712,10 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
     const int gbase = kap * a.GW, q = tid & 127, blk = q >> 5, j = 4 * (q & 31);
     const int chn = gbase + (blk == 0 ? j : blk == 1 ? D + j : blk == 2 ? 2 * D + hh * D + j
                                                       : 2 * D + a.r * D + hh * D + j);
+    // the gate inputs first (even threads b, odd threads a of token tid / 2): their loads
+    // then return before the threads' own token outputs, not a round trip after them
+    const float yg = tid < 2 * Tk ? proj_one(a, seq * Tk + (tid >> 1), a.Nq + kap * 2 * a.r + ((tid & 1) ? a.r : 0) + hh)
+                                  : 0.0f;
 #pragma unroll 1
     for (int p0 = 0; p0 < Tk; p0 += 2 * kVerPasses) {
       f32x4_t v[kVerPasses];
@@ -1711,12 +1725,11 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
 #pragma unroll
       for (int u = 0; u < kVerPasses; ++u) {
         const int t = p0 + 2 * u + (tid >> 7);
-        if (t < Tk) *reinterpret_cast<f32x4_t*>(&sh.y[t][blk][j]) = v[u];
+        if (t < Tk) *reinterpret_cast<f32x4_t*>(&sh.y[t].b[blk][j]) = v[u];
       }
     }
-    if (tid < 2 * Tk) {  // even threads beta, odd threads a_t of token tid / 2
+    if (tid < 2 * Tk) {
       const int t = tid >> 1;
-      const float yg = proj_one(a, seq * Tk + t, a.Nq + kap * 2 * a.r + ((tid & 1) ? a.r : 0) + hh);
       if (tid & 1) {
         const float x = yg + dtb;
         const float sp = x > 20.0f ? x : __logf(1.0f + __expf(x));
@@ -1726,8 +1739,16 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
       }
     }
     if (tid >= 192 && tid < 192 + Tk) sh.dst[tid - 192] = a.dst[seq * Tk + tid - 192];
+    // past every wait of this workgroup: count it (the atomic's return is waited for at
+    // once, after this wave's loads; taken at the end instead, its wait there would also
+    // wait for the snapshot stores before the last workgroup clears the counters: measured)
     if (tid == 128) exit_ticket = add_agent(sy(a, kSyExit), 1u);
   }
+  // Nothing is in flight here (every load above has been consumed). Saying so explicitly
+  // tells the compiler that the old state's registers are ready: otherwise its first use
+  // (the matrix-core operands, after the conv-window stores below) gets a wait for every
+  // memory operation before it, those stores included (measured: a write round trip).
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   TRACE_POINT(14);
 
@@ -1737,9 +1758,9 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
   if (qk_thread) {
 #pragma unroll 1
     for (int t = 0; t < Tk; ++t) {
-      const float yq = sh.y[t][0][tid], yk = sh.y[t][1][tid];
-      sh.y[t][0][tid] = conv_out(c0c, yq);
-      sh.y[t][1][tid] = conv_out(c1c, yk);
+      const float yq = sh.y[t].b[0][tid], yk = sh.y[t].b[1][tid];
+      sh.y[t].b[0][tid] = conv_out(c0c, yq);
+      sh.y[t].b[1][tid] = conv_out(c1c, yk);
       const int ds = sh.dst[t];
       if (qk_owner && ds > 0 && ds < a.slots) {
         conv_store(a, ds, c0c, yq);
@@ -1752,8 +1773,8 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
     const int j = tid - D;
 #pragma unroll 1
     for (int t = 0; t < Tk; ++t) {
-      const float yv = sh.y[t][2][j];
-      sh.y[t][2][j] = conv_out(c0c, yv);
+      const float yv = sh.y[t].b[2][j];
+      sh.y[t].b[2][j] = conv_out(c0c, yv);
       const int ds = sh.dst[t];
       if (ds > 0 && ds < a.slots) conv_store(a, ds, c0c, yv);
       conv_roll(c0c, yv);
@@ -1762,60 +1783,9 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
   __syncthreads();
   TRACE_POINT(2);
 
-  // S0^T k_t, then S0^T q_t, over this wave's 64 rows for all tokens: A operand = token
-  // (lane & 15)'s k (or q) at the same 8 rows as the B operand's K index. Lane l's result
-  // holds, for token 4 (l >> 4) + i, the columns c0 .. c0 + 3 (one per j): the upper row
-  // half's waves store theirs, then the lower half's add theirs to them.
   const int ta = lane & 15;
   const bool tok = ta < Tk;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int pr = 0; pr < 2; ++pr) {  // pr 0: k (y block 1, into u); pr 1: q (block 0, into w)
-    f32x4_t acc[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int m0 = 0; m0 < 16; m0 += 8) {
-      const u32x4_t av = tok ? bf16x8_of(&sh.y[ta][1 - pr][r0 + m0]) : zero;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // column j, rows m0 .. m0 + 7: a bf16 pool's halves as they are; an f32 element as
-        // hi + lo, both bf16 values
-        auto hi = [&](int i) { return rbf(S[m0 + i][j]); };
-        auto lo = [&](int i) { return rbf(S[m0 + i][j] - rbf(S[m0 + i][j])); };
-        auto col2 = [&](int i) {  // rows m0 + i, m0 + i + 1 of column j of a bf16 pool
-          const uint32_t x = Sb[m0 + i][j >> 1], y = Sb[m0 + i + 1][j >> 1];
-          return (j & 1) ? (x >> 16) | (y & 0xffff0000u) : (x & 0xffffu) | (y << 16);
-        };
-        u32x4_t bh;
-        if constexpr (kF32)
-          bh = u32x4_t{bf16_pair(hi(0), hi(1)), bf16_pair(hi(2), hi(3)), bf16_pair(hi(4), hi(5)),
-                       bf16_pair(hi(6), hi(7))};
-        else
-          bh = u32x4_t{col2(0), col2(2), col2(4), col2(6)};
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bh), acc[j], 0, 0, 0);
-        if constexpr (kF32) {
-          const u32x4_t bl = {bf16_pair(lo(0), lo(1)), bf16_pair(lo(2), lo(3)), bf16_pair(lo(4), lo(5)),
-                              bf16_pair(lo(6), lo(7))};
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bl), acc[j], 0, 0, 0);
-        }
-      }
-    }
-    float(*dst)[128] = pr == 0 ? sh.u : sh.w;
-    if (rh == 1) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<f32x4_t*>(&dst[4 * rg + i][c0]) = f32x4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-    }
-    __syncthreads();
-    if (rh == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4_t* pd = reinterpret_cast<f32x4_t*>(&dst[4 * rg + i][c0]);
-        *pd = *pd + f32x4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-      }
-    }
-  }
   // the tokens' dot products, one product per wave: k.k, q.k, q.q (16x16, tokens past Tk zero)
   if (wave < 3) {
     const int xa = wave == 0 ? 1 : 0, xb = wave == 2 ? 0 : 1;  // blocks: q 0, k 1
@@ -1823,8 +1793,8 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
 #pragma unroll
     for (int s4 = 0; s4 < D / 32; ++s4) {
       const int k0 = 32 * s4 + 8 * rg;
-      const u32x4_t va = tok ? bf16x8_of(&sh.y[ta][xa][k0]) : zero;
-      const u32x4_t vb = tok ? bf16x8_of(&sh.y[ta][xb][k0]) : zero;
+      const u32x4_t va = tok ? bf16x8_of(&sh.y[ta].b[xa][k0]) : zero;
+      const u32x4_t vb = tok ? bf16x8_of(&sh.y[ta].b[xb][k0]) : zero;
       g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(vb), g, 0, 0, 0);
     }
 #pragma unroll
@@ -1837,7 +1807,63 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
       }
     }
   }
+  // S0^T k_t and S0^T q_t over this wave's 64 rows for all tokens: A operand = token
+  // (lane & 15)'s k (or q) at the same 8 rows as the B operand's K index. Lane l's results
+  // hold, for token 4 (l >> 4) + i, the columns c0 .. c0 + 3 (one per j): the upper row
+  // half's waves store theirs, then the lower half's add theirs to them.
+  f32x4_t acc[2][4];
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[pr][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int m0 = 0; m0 < 16; m0 += 8) {
+    const u32x4_t ak = tok ? bf16x8_of(&sh.y[ta].b[1][r0 + m0]) : zero;
+    const u32x4_t aq = tok ? bf16x8_of(&sh.y[ta].b[0][r0 + m0]) : zero;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // column j, rows m0 .. m0 + 7: a bf16 pool's halves as they are; an f32 element as
+      // hi + lo, both bf16 values
+      auto hi = [&](int i) { return rbf(S[m0 + i][j]); };
+      auto lo = [&](int i) { return rbf(S[m0 + i][j] - rbf(S[m0 + i][j])); };
+      auto col2 = [&](int i) {  // rows m0 + i, m0 + i + 1 of column j of a bf16 pool
+        const uint32_t x = Sb[m0 + i][j >> 1], y = Sb[m0 + i + 1][j >> 1];
+        return (j & 1) ? (x >> 16) | (y & 0xffff0000u) : (x & 0xffffu) | (y << 16);
+      };
+      u32x4_t bh;
+      if constexpr (kF32)
+        bh = u32x4_t{bf16_pair(hi(0), hi(1)), bf16_pair(hi(2), hi(3)), bf16_pair(hi(4), hi(5)), bf16_pair(hi(6), hi(7))};
+      else
+        bh = u32x4_t{col2(0), col2(2), col2(4), col2(6)};
+      acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ak), as_bf16x8(bh), acc[0][j], 0, 0, 0);
+      acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aq), as_bf16x8(bh), acc[1][j], 0, 0, 0);
+      if constexpr (kF32) {
+        const u32x4_t bl = {bf16_pair(lo(0), lo(1)), bf16_pair(lo(2), lo(3)), bf16_pair(lo(4), lo(5)),
+                            bf16_pair(lo(6), lo(7))};
+        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ak), as_bf16x8(bl), acc[0][j], 0, 0, 0);
+        acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(aq), as_bf16x8(bl), acc[1][j], 0, 0, 0);
+      }
+    }
+  }
+  if (rh == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<f32x4_t*>(&sh.u[4 * rg + i][c0]) = f32x4_t{acc[0][0][i], acc[0][1][i], acc[0][2][i], acc[0][3][i]};
+      *reinterpret_cast<f32x4_t*>(&sh.w[4 * rg + i][c0]) = f32x4_t{acc[1][0][i], acc[1][1][i], acc[1][2][i], acc[1][3][i]};
+    }
+  }
   __syncthreads();
+  // the lower row half's waves complete the sums; in the same phase, the coefficient tables
+  // (they touch other arrays)
+  if (rh == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4_t* pu = reinterpret_cast<f32x4_t*>(&sh.u[4 * rg + i][c0]);
+      f32x4_t* pw = reinterpret_cast<f32x4_t*>(&sh.w[4 * rg + i][c0]);
+      *pu = *pu + f32x4_t{acc[0][0][i], acc[0][1][i], acc[0][2][i], acc[0][3][i]};
+      *pw = *pw + f32x4_t{acc[1][0][i], acc[1][1][i], acc[1][2][i], acc[1][3][i]};
+    }
+  }
   {  // the coefficient tables, one (t, j) per thread
     const int t = tid >> 4, j = tid & 15;
     if (t < Tk && j < Tk) {
@@ -1877,7 +1903,7 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
         float acc = sh.gc[t] * (sh.u[t][c] * sh.ks[t]);
 #pragma unroll
         for (int j = 0; j < t; ++j) acc = fmaf(sh.kk[t][j], dr[j], acc);
-        dr[t] = sh.gt[t][0] * (sh.y[t][2][c] - acc);
+        dr[t] = sh.gt[t][0] * (sh.y[t].b[2][c] - acc);
         float o = sh.gc[t] * (sh.w[t][c] * sh.qs[t]);
 #pragma unroll
         for (int j = 0; j <= t; ++j) o = fmaf(sh.qk[t][j], dr[j], o);
@@ -1902,8 +1928,8 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
       ss += dpp<0x141>(ss);  // the other quad among 8 (mirror)
       ss += dpp<0x128>(ss);  // the other 8 among 16 (rotate by 8)
       const float rstd = __builtin_amdgcn_rsqf(ss * (1.0f / (float)D) + a.geps);
-      const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(&sh.y[t][3][8 * p16]);
-      const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(&sh.y[t][3][8 * p16 + 4]);
+      const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(&sh.y[t].b[3][8 * p16]);
+      const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(&sh.y[t].b[3][8 * p16 + 4]);
       auto gated = [&](float o, float z, uint32_t g, int hi) {
         return o * rstd * bf2f((uint16_t)(hi ? g >> 16 : g)) * silu(z);
       };
@@ -1935,7 +1961,7 @@ __device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
   };
   auto tok_load = [&](int t, TokIn& v) {
 #pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) v.k[m4] = *reinterpret_cast<const f32x4_t*>(&sh.y[t][1][r0 + 4 * m4]);
+    for (int m4 = 0; m4 < 4; ++m4) v.k[m4] = *reinterpret_cast<const f32x4_t*>(&sh.y[t].b[1][r0 + 4 * m4]);
     v.d = *reinterpret_cast<const f32x4_t*>(&sh.u[t][c0]);
     v.dec = sh.gt[t][1];
     v.kst = sh.ks[t];
