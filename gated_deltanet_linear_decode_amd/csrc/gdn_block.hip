@@ -211,6 +211,11 @@ __device__ __forceinline__ uint32_t add_agent(uint32_t* p, uint32_t v) {
 // this wave's loads have returned and its stores have completed (so a counter bumped
 // after them is seen after them)
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15). As
+// a builtin (not asm) the compiler's own wait placement sees it: registers loaded before it
+// are then known ready, where it would otherwise wait for every memory operation in flight
+// at their first use, stores included.
+constexpr int kWaitVm0 = 0x0F70;
 // 16-byte store coherent at agent scope (the vector form of st_agent)
 __device__ __forceinline__ void st_agent16(uint32_t* p, u32x4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
@@ -1458,6 +1463,11 @@ __device__ void rec_role(const Args& a, int rb, RecShared& sh) {
         }
       }
       TRACE_POINT(8);
+      // Nothing is in flight here in a single-token step (the projection outputs, gate
+      // inputs and exit ticket have all been used). Said explicitly, the conv window and
+      // state registers are known ready, so the conv-window stores below are not waited for
+      // before the state pass (measured: a write round trip for the whole workgroup).
+      if constexpr (!MULTI) __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       TRACE_POINT(9);
       const int ty = MULTI ? t : 0;
@@ -1605,8 +1615,6 @@ struct TokRows {
   float pad[4];
 };
 constexpr int kURow = 132;  // padded row of u and w, for the same reason
-// s_waitcnt immediate for vmcnt(0) alone (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15)
-constexpr int kWaitVm0 = 0x0F70;
 struct VerShared {
   TokRows y[GDN_MAX_ROWS];        // per token: projections q, k, v, z; then q, k, v conv outputs
   float u[GDN_MAX_ROWS][kURow];   // S0^T k_t (k not normalised), then d_t
