@@ -334,6 +334,7 @@ struct Args {
   int PW;      // floats per row of the split partials: Nq + Nb rounded up to whole 128-byte lines
   int spin;    // poll limit of every bounded wait
   int mx_ceil; // MXFP4 activation scale rule: 0 rounded maximum, 1 ceiling
+  int wlds;    // bf16 projections fetch their last weight steps into LDS at launch (1) or not
   float eps, l2eps, geps;
 };
 
@@ -595,9 +596,11 @@ constexpr int kXPad = 8;    // bf16 of padding per LDS row, so that the 16 rows 
 constexpr int kMxRow = kKr / 2 + 16;         // LDS bytes per row of MXFP4 codes (padded)
 constexpr int kMxScBase = GDN_MAX_ROWS * kMxRow;  // LDS byte offset of the MXFP4 scale rows
 
+constexpr int kLdsSteps = 4;  // bf16 weight steps per wave fetched straight into LDS at launch
 struct ProjShared {
   uint16_t xs[GDN_MAX_ROWS][kKr + kXPad];  // the activation slice [decode row][k], or MXFP4 image bytes
   float red[4][256];
+  u32x4_t wl[4][kLdsSteps][64];  // per wave: the last kLdsSteps weight steps of its range
 };
 
 // the 4 waves' accumulators of one tile -> the tile's split partials (fixed-order sum over
@@ -887,6 +890,16 @@ __device__ void proj_bf16(const Args& a, int gb, int t0, int s, ProjShared& sh) 
 #pragma unroll
   for (int u = 0; u < kWin; ++u)
     if (u < nsteps) w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, s, lstep(u), lane));
+  // The last P steps of the range go straight into LDS now, so that they stream during the
+  // wait for the activations (the register window holds only kWin steps: deeper register
+  // windows cost occupancy, measured) and the stream left after the wait is P steps shorter.
+  const int P = TILES && a.wlds && nsteps >= kWin + 2 * kLdsSteps ? kLdsSteps : 0;
+  const int nreg = nsteps - P;  // steps through the register window
+#pragma unroll
+  for (int p = 0; p < kLdsSteps; ++p)
+    if (p < P)
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)wptr<PACKED>(a, t, s, lstep(nreg + p), lane),
+                                       (__attribute__((address_space(3))) void*)&sh.wl[wave][p][0], 16, 0, 0);
 
   if (a.normed)
     xin_store(a, xi, sh);
@@ -899,15 +912,22 @@ __device__ void proj_bf16(const Args& a, int gb, int t0, int s, ProjShared& sh) 
     return *reinterpret_cast<const u32x4_t*>(&sh.xs[xrow][32 * lstep(i) + 8 * (lane >> 4)]);
   };
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int i0 = 0; i0 < nsteps; i0 += kWin) {
+  for (int i0 = 0; i0 < nreg; i0 += kWin) {
 #pragma unroll
     for (int u = 0; u < kWin; ++u) {
       const int i = i0 + u;
-      if (i < nsteps) {
+      if (i < nreg) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[u]), as_bf16x8(xload(i)), acc, 0, 0, 0);
-        if (i + kWin < nsteps) w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, s, lstep(i + kWin), lane));
+        if (i + kWin < nreg) w[u] = __builtin_nontemporal_load(wptr<PACKED>(a, t, s, lstep(i + kWin), lane));
       }
     }
+  }
+  if (P) {
+    wait_stores();  // vmcnt(0): the wave's LDS fills have landed (issued before every refill above)
+#pragma unroll
+    for (int p = 0; p < kLdsSteps; ++p)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(sh.wl[wave][p][lane]), as_bf16x8(xload(nreg + p)), acc, 0,
+                                                    0, 0);
   }
   TRACE_POINT(2);
   if (TILES)
@@ -2286,6 +2306,7 @@ struct gdn_block {
   int nq, nb, cd, tq, tb, t, splits, steps, sync_words;
   int pw;             // floats per row of the split partials (whole 128-byte lines)
   int spin;           // poll limit of the bounded waits
+  int cus;            // compute units of the device
   int kr;             // K range of a projection workgroup
   bool fold;          // out_proj folded in
   int o, ko;          // out_proj workgroups (4 tiles of 16 columns of H each) and K (nv * dv)
@@ -2490,6 +2511,7 @@ extern "C" int gdn_block_create(const gdn_block_config* cfg, gdn_block_t* out) {
   const size_t o_sync = take((size_t)b->sync_words * 4);
 
   hipError_t e = hipGetDevice(&b->device);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&b->cus, hipDeviceAttributeMultiprocessorCount, b->device);
   if (e == hipSuccess) e = hipMalloc(&b->scratch, off);
   if (e == hipSuccess) e = hipMemset(b->scratch, 0, off);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -2690,6 +2712,10 @@ int decode_impl(gdn_block* b, const Scratch& sc, const void* x, void* residual, 
   a.PW = b->pw;
   a.spin = b->spin;
   a.mx_ceil = c.mx_scale_rule == GDN_MXSCALE_CEIL ? 1 : 0;
+  // The LDS fetch at launch pays when the projection workgroups all start at once (up to 2
+  // per compute unit) and wait for the activations together; a larger grid streams in
+  // several rounds with no such wait to hide (measured slower there).
+  a.wlds = a.G <= 2 * b->cus ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   // no norm workgroups with a normed input; the out_proj workgroups last
