@@ -32,7 +32,7 @@ POINTS = {
     "proj": {0: "start", 1: "activations staged", 2: "matrix-core work done", 3: "partials published"},
     "rec": {0: "start", 1: "waits done", 5: "partials loaded", 8: "gates computed", 9: "barrier",
             2: "conv done", 10: "state pass", 6: "row-group butterfly", 11: "d and o", 7: "state update issued",
-            12: "gated-norm sum", 3: "core row stored", 4: "end", 13: "verify: token outputs loading",
+            12: "gated-norm sum", 3: "core row stored", 4: "end", 13: "token outputs: loads issued",
             14: "token loop start"},
     "oproj": {0: "start", 1: "core rows seen", 2: "matrix-core work done", 3: "out rows stored"},
 }
