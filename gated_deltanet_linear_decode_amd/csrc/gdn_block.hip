@@ -5,16 +5,19 @@
 // (the front of a GDN layer as one launch, "sgl-amd-mono PR #89", Modifications; the
 // "GDN block" of "vLLM PR #60833", Details / Launches):
 //
-//   [0, R*P)          norm: P = ceil(H / 2048) workgroups per row (none when x is already
-//                     normed). Each loads the whole row, forms h = bf16(x + residual) and
-//                     the row's rstd (all P in the same order, so with the same result), and
-//                     publishes one 2048-wide slice of xn = bf16(h * rstd * (1 + w)) to
-//                     scratch; then it counts itself done and rewrites its slice of the
-//                     residual row with h (with a residual input, once every norm workgroup
-//                     has loaded its row). No workgroup holds x in LDS; every projection
-//                     workgroup reads the finished xn ("vLLM PR #60833", Details / x without
-//                     an LDS tile). With MXFP4 in_proj_qkvz the slice is also quantised to
-//                     MXFP4 (codes + one e8m0 scale per 32) into a second scratch image.
+//   [0, R*P)          norm. bf16 and MXFP6 in_proj_qkvz: one workgroup per row (P = 1)
+//                     loads the row, forms h = bf16(x + residual) and the row's rstd, and
+//                     publishes only the rstd (a word that is never 0, so its own ready
+//                     flag); then it rewrites the residual row with h, with a residual
+//                     input once every projection workgroup has counted that it loaded its
+//                     slice of the row. MXFP4: P = ceil(H / 2048) workgroups per row each
+//                     load the whole row (all P sum it in the same order, so with the same
+//                     rstd), convert one 2048-wide slice to xn = bf16(h * rstd * (1 + w))
+//                     and quantise it to MXFP4 (codes + one e8m0 scale per 32) into a
+//                     scratch image, count themselves done and rewrite their residual slice.
+//                     No workgroup holds x in LDS ("vLLM PR #60833", Details / x without an
+//                     LDS tile). With x already normed there are no norm workgroups, except
+//                     MXFP4 past 2 rows: P quantiser workgroups per row make the image.
 //   [R*P, R*P+G)      projection: in_proj_qkvz and in_proj_ba as one skinny GEMM on the
 //                     matrix cores: bf16 weights on v_mfma_f32_16x16x32_bf16, MXFP4 weights
 //                     on v_mfma_scale_f32_16x16x128_f8f6f4 (fp4 x fp4 with per-32 scales),
@@ -22,33 +25,37 @@
 //                     on the bf16 instruction with the bf16 activations;
 //                     16 weight rows x 16 decode rows per instruction. A workgroup owns one
 //                     K range and 4 in_proj_qkvz tiles (one per wave) or one in_proj_ba tile.
-//                     It issues its weight loads first, then waits for the norm rows, stages
-//                     the activations of its K range in LDS once, multiplies, and publishes
-//                     its f32 partial sums; then it counts itself done for the tiles'
-//                     key-head group (or for the b|a tiles).
+//                     It issues its weight loads first (bf16: its last 4 K steps straight
+//                     into LDS as well), with bf16 and MXFP6 also the loads of its K range of
+//                     x and residual, then waits for the rows' rstd (or the MXFP4 image),
+//                     stages the activations of its K range in LDS once, multiplies, and
+//                     publishes its f32 partial sums; then it counts itself done for the
+//                     tiles' key-head group (or for the b|a tiles).
 //   [.., +Rs*nv)      recurrence: one workgroup per (sequence, value head); a decode call
 //                     has one token per sequence, a verify call several. It loads its
 //                     dk x dv state tile and its conv state and taps first, waits for its
 //                     key-head group and the b|a tiles, adds the split partials of its
 //                     channels in split order and rounds them to bf16 (the projection
 //                     output), runs the causal conv update + SiLU, L2 norms, gates, the gated
-//                     delta rule, the state store and the gated RMSNorm into the core output,
-//                     token after token. The q|k conv state of a key head is shared by its r
-//                     value heads: the last of them writes it once the others have read the
-//                     old rows.
+//                     delta rule, the state store and the gated RMSNorm into the core output.
+//                     A verify step at head dim 128 evaluates its tokens in the chunked form
+//                     of the recurrence (rec_verify); below 128 it runs them one after the
+//                     other. The q|k conv state of a key head is shared by its r value heads:
+//                     the last of them writes it once the others have read the old rows.
 //   [.., +H/64)       out_proj (folded in, optional): 4 tiles of 16 hidden columns per
 //                     workgroup; the weights stream from launch start, the core rows are
 //                     multiplied once every recurrence workgroup has stored its row.
 //
-// Every wait ends: projection, recurrence and out_proj workgroups wait only for workgroups
-// with lower block ids, which the dispatcher starts first, and a norm workgroup's one wait
-// (before its residual rewrite) is for the other norm workgroups, which count themselves
-// before they wait for anything. Each wait is also bounded and records a sticky error
-// word if it gives up. Data handed from one workgroup to another travels as agent-scope atomic
-// stores (coherent across the XCDs' L2s, one access at a time) followed by a wait for
-// the stores; readers poll counters with agent-scope atomic loads. No device-wide fence
-// is used: on gfx950 one writes back and invalidates a whole L2. Every counter is
-// cleared by the last workgroup that reads it, so the next launch starts from zero.
+// Every wait ends. Projection, recurrence and out_proj workgroups wait only for workgroups
+// with lower block ids, which the dispatcher starts first. A norm workgroup's one wait
+// (before its residual rewrite) is for workgroups that count themselves before any wait of
+// their own and never wait for that rewrite: the projection workgroups, right after loading
+// their slice (bf16, MXFP6), or the other norm workgroups (MXFP4). Each wait is also bounded
+// and records a sticky error word if it gives up. Data handed from one workgroup to another
+// travels as agent-scope stores (coherent across the XCDs' L2s) followed by a wait for the
+// stores; readers poll counters with agent-scope atomic loads. No device-wide fence is used:
+// on gfx950 one writes back and invalidates a whole L2. Every counter is cleared by the
+// last workgroup that reads it, so the next launch starts from zero.
 //
 // Every reduction runs in a fixed order that does not depend on the row count, so a
 // row's results do not change with the other rows (batch invariance, "sgl-amd-mono PR
