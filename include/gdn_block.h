@@ -130,7 +130,9 @@ typedef struct gdn_block_config {
                               "SGLang PR #43558", Modifications): steps 1 (residual add and
                               norm) are skipped, residual and norm_w are neither read nor
                               written (they may be NULL), has_residual must be 0; with MXFP4
-                              each projection workgroup quantises its K range of xn itself */
+                              each projection workgroup quantises its K range of xn itself
+                              up to 2 rows, and from 3 rows the launch quantises each row
+                              once (the same codes and scales either way) */
   int32_t fold_out_proj;   /* 1: the launch also writes the rank's out_proj partial
                               out = bf16(core W_out^T), [R, H] ("SGLang PR #43558",
                               Modifications: K1 with out_proj folded in); needs nv*dv a
