@@ -1669,7 +1669,7 @@ __device__ __forceinline__ u32x4_t bf16x8_of(const float* p) {
 // (Its profiling-build timeline points are few on purpose: more of them made that build of
 // the role spill registers, which distorts the timeline.)
 template <typename ST>
-__device__ void rec_verify(const Args& a, int rb, VerShared& sh) {
+__device__ __forceinline__ void rec_verify(const Args& a, int rb, VerShared& sh) {
   constexpr int D = 128;
   constexpr bool kF32 = sizeof(ST) == 4;
   // State tile layout: wave w holds the column half ch = w & 1 and the row half rh = w >> 1;
@@ -2121,6 +2121,20 @@ __device__ void oproj_role(const Args& a, int ob, ProjShared& sh) {
 
 // ---------------------------------------------------------------------------------------
 
+// The launch arguments read through an address the compiler cannot see through (the kernel's
+// argument segment, where Args is the only argument, passed through an empty asm): the
+// fields a role reads are then loaded inside that role. Read through the parameter itself,
+// the compiler may load them all at the kernel's entry, and the values the other roles need
+// stay live in scalar registers across the whole role: in the multi-token launches that
+// spilled scalar registers to a stack frame. The one-token launches, which have no spills,
+// keep the parameter.
+__device__ __forceinline__ const Args& role_args() {
+  using KArgs = const __attribute__((address_space(4))) Args*;
+  KArgs p = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const Args*)p;
+}
+
 // FOLD is a template flag, not only a launch argument, so that the out_proj role's register
 // tile does not raise the register count (and lower the occupancy) of the launches without it.
 template <bool PACKED, int FMT, int DK, typename ST, bool FOLD, bool MULTI, bool DST = false>
@@ -2146,7 +2160,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Args a) {
     proj_role<PACKED, FMT>(a, b - nn, sh.proj);
   } else if (b < nn + a.G + nr) {
     if constexpr (kChunked)
-      rec_verify<ST>(a, b - nn - a.G, sh.rec);
+      rec_verify<ST>(role_args(), b - nn - a.G, sh.rec);
+    else if constexpr (MULTI)  // (inlined as before: not by itself once the asm is there)
+      [[clang::always_inline]] rec_role<DK, ST, MULTI, DST>(role_args(), b - nn - a.G, sh.rec);
     else
       rec_role<DK, ST, MULTI, DST>(a, b - nn - a.G, sh.rec);
   } else if (FOLD) {
