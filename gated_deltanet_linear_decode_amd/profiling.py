@@ -4,6 +4,9 @@
     python -m gated_deltanet_linear_decode_amd.profiling run --raw gpurun_out/prof
     python -m gated_deltanet_linear_decode_amd.profiling summarize --raw gpurun_out/prof --profiles profiles
 
+    python -m gated_deltanet_linear_decode_amd.profiling run --raw gpurun_out/prof --verify 1x4,4x4
+    python -m gated_deltanet_linear_decode_amd.profiling summarize --raw gpurun_out/prof --verify 1x4,4x4
+
 `run` profiles bench.py (a child process per profile; this process never touches the GPU)
 for each workload in WORKLOADS: a kernel trace with statistics; the HBM byte counters
 FETCH_SIZE and WRITE_SIZE, one pass each; one pass of matrix-core counters; and the
@@ -11,7 +14,8 @@ in-kernel timeline of the profiling build. It also profiles a plain 256 MiB devi
 whose counter readings scale FETCH_SIZE and WRITE_SIZE to bytes. `summarize` turns the
 CSV files into one markdown summary per workload and profile, and profiles/hbm_traffic.json
 (bytes per launch, which bench.py reports as roofline.traffic while the kernel source is
-unchanged).
+unchanged). With `--verify SxT,...` both take only kernel traces of verify steps (S sequences
+of T tokens on the headline shape) instead.
 """
 from __future__ import annotations
 
@@ -81,10 +85,27 @@ def commands(raw: str, workloads=None):
     return out
 
 
-def run(raw: str, workloads=None) -> None:
+VERIFY_CONFIG = "tp8_rank_bf16_state_layer0"
+
+
+def verify_commands(raw: str, steps):
+    """(name, argv, timeout seconds) of a kernel trace per verify step (seqs, tokens): bench.py
+    times the step as in its verify sweep, after a short headline run."""
+    out = []
+    for seqs, tokens in steps:
+        argv = ["python3", os.path.join(ROOT, "bench.py"), "--config", VERIFY_CONFIG, "--rows", "1", "--steps", "48",
+                "--warmup", "8", "--sweep-rows", "", "--workloads", "", "--verify", f"{seqs}x{tokens}",
+                "--sweep-steps", "960", "--no-cpu-baseline"]
+        name = f"kt_verify_{seqs}x{tokens}"
+        out.append((name, ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+                           os.path.join(raw, name), "-o", "run", "--", *argv], 400))
+    return out
+
+
+def run(raw: str, workloads=None, verify=None) -> None:
     os.makedirs(raw, exist_ok=True)
     env = dict(os.environ, TMPDIR="/tmp")
-    for name, argv, limit in commands(raw, workloads):
+    for name, argv, limit in (verify_commands(raw, verify) if verify else commands(raw, workloads)):
         print(f"[profiling] {name}", flush=True)
         log = os.path.join(raw, f"{name}.log")
         with open(log, "w") as f:
@@ -203,16 +224,51 @@ def summarize(raw: str, profiles: str, workloads=None) -> None:
         json.dump(traffic, f, indent=1)
 
 
+def summarize_verify(raw: str, profiles: str, steps) -> None:
+    sys.path.insert(0, ROOT)
+    from gated_deltanet_linear_decode_amd import configs
+    shape = configs.ALL[VERIFY_CONFIG]
+    foot = f"Kernel source hash (sha256 of gdn_block.hip, first 16 hex digits): {kernel_source_hash()}.\n"
+    cmds = {name: argv for name, argv, _ in verify_commands(raw, steps)}
+    for seqs, tokens in steps:
+        name = f"kt_verify_{seqs}x{tokens}"
+        st = _rows(os.path.join(raw, name, "run_kernel_stats.csv"))
+        # decode_kernel<PACKED, FMT, DK, ST, FOLD, MULTI, DST>: the verify step's instantiation
+        # has MULTI set (or DST, for one token at head dim 128); the headline run's has neither
+        ver = [r for r in st if "decode_kernel" in r["Name"] and not _short(r["Name"]).endswith("false, false>")]
+        assert len(ver) == 1, [r["Name"] for r in st]
+        us = float(ver[0]["AverageNs"]) / 1000
+        algo = configs.algorithmic_bytes_verify(shape, seqs, tokens)
+        gbs = algo / (us * 1e-6) / 1e9
+        lines = [f"# decode_kernel, verify step of {seqs} x {tokens} tokens ({VERIFY_CONFIG}): kernel trace", "",
+                 "Command (run from /tmp with TMPDIR=/tmp; <repo> is the repository root):", "", "```",
+                 _cmd_text(cmds[name]), "```", "",
+                 "| kernel | calls | average ns | min ns | max ns | share of GPU time |", "|---|---|---|---|---|---|"]
+        for r in st:
+            lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                         f"{r['MaxNs']} | {float(r['Percentage']):.2f} % |")
+        lines += ["", f"The verify launch (`{_short(ver[0]['Name'])}`): {us:.2f} µs on average; algorithmic bytes "
+                      f"per launch {algo:,}, so {gbs:.0f} GB/s = {gbs / HBM_PEAK_GBS:.3f} of 8 TB/s. The decode "
+                      "launches with MULTI and DST unset are the short headline run before the verify sweep; the "
+                      "other kernels are set-up work outside the timed graphs.", foot]
+        with open(os.path.join(profiles, f"decode_kernel_verify_{seqs}x{tokens}_kernel_trace.md"), "w") as f:
+            f.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("action", choices=["run", "summarize"])
     ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof"))
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--only", default="", help="comma-separated workload:rows pairs (default: every workload)")
+    ap.add_argument("--verify", default="", help="comma-separated verify steps SxT: kernel traces of these only")
     a = ap.parse_args()
     wl = [(w.split(":")[0], int(w.split(":")[1])) for w in a.only.split(",") if w] or None
+    ver = [tuple(int(v) for v in p.split("x")) for p in a.verify.split(",") if p]
     if a.action == "run":
-        run(os.path.abspath(a.raw), wl)
+        run(os.path.abspath(a.raw), wl, ver)
+    elif ver:
+        summarize_verify(os.path.abspath(a.raw), os.path.abspath(a.profiles), ver)
     else:
         summarize(os.path.abspath(a.raw), os.path.abspath(a.profiles), wl)
 
