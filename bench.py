@@ -170,6 +170,48 @@ class VerifyRotation(Rotation):
                         weights_struct=c["wsp"] if packed else c["ws"])
 
 
+def time_read_stream(nbytes, copies, steps, warmup):
+    """µs per launch of the plain read stream (gdn_read_stream) over `nbytes`, timed like the
+    block: graphs of launches rotating over `copies` buffers of that size (past the MALL)."""
+    import torch
+
+    from gated_deltanet_linear_decode_amd import abi
+    n = (nbytes + 15) // 16 * 16
+    bufs = [torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
+    sinks = torch.empty(copies, (n + 32767) // 32768, dtype=torch.int32, device="cuda:0")
+
+    def launch(i):
+        abi.gdn_read_stream(bufs[i % copies].data_ptr(), n, sinks[i % copies].data_ptr(),
+                            torch.cuda.current_stream().cuda_stream)
+
+    per = 4 * copies
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(copies):
+            launch(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per):
+            launch(i)
+    reps = max(1, steps // per)
+    for _ in range(max(1, warmup // per)):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1000.0 / (reps * per)
+    del bufs, sinks, g
+    torch.cuda.empty_cache()
+    return n, us
+
+
 def sweep_verify(shape, pairs, steps):
     """µs per verify launch for each (sequences, tokens) pair."""
     out = {}
@@ -317,6 +359,10 @@ def main():
     pairs = [tuple(int(v) for v in p.split("x")) for p in args.verify.split(",") if p]
     verify = sweep_verify(shape, pairs, args.sweep_steps) if pairs else {}
 
+    stream_bytes, stream_us = time_read_stream(algo, shape.layers, args.sweep_steps, args.sweep_steps // 4)
+    stream_gbs = stream_bytes / (stream_us * 1e-6) / 1e9
+    log(f"read stream of {stream_bytes} bytes: {stream_us:.2f} us/launch, {stream_gbs:.0f} GB/s")
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -356,6 +402,11 @@ def main():
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algo_bytes_per_launch": algo, "kernel": "decode_kernel (the whole block, one launch)",
+        },
+        "read_stream": {
+            "bytes": stream_bytes, "us": round(stream_us, 3), "gbs": round(stream_gbs, 1),
+            "frac_of_peak": round(stream_gbs / HBM_PEAK_GBS, 4), "decode_frac_of_stream": round(gbs / stream_gbs, 4),
+            "kernel": "read_stream_kernel (gdn_read_stream: one plain read of the launch's algorithmic bytes)",
         },
         "sweep": sweep,
         "workloads": workloads,

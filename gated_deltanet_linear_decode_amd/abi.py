@@ -27,7 +27,7 @@ GDN_MAX_ROWS = 16
 EXPORTED = ("gdn_block_create", "gdn_block_decode", "gdn_block_destroy", "gdn_block_last_error",
             "gdn_block_packed_weight_bytes", "gdn_block_pack_weights", "gdn_block_check",
             "gdn_mxfp4_quantize", "gdn_block_decode_with_out_proj", "gdn_mxfp6_round_weights",
-            "gdn_block_verify", "gdn_block_set_spin_limit", "gdn_block_decode_noalloc")
+            "gdn_block_verify", "gdn_block_set_spin_limit", "gdn_block_decode_noalloc", "gdn_read_stream")
 
 
 class GdnBlockConfig(ctypes.Structure):
@@ -99,6 +99,8 @@ def load() -> ctypes.CDLL:
         lib.gdn_block_verify.argtypes = [c_void_p, c_void_p, c_void_p, POINTER(GdnBlockWeights), c_void_p, c_void_p,
                                          c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]
         lib.gdn_block_verify.restype = c_int
+        lib.gdn_read_stream.argtypes = [c_void_p, c_size_t, c_void_p, c_void_p]
+        lib.gdn_read_stream.restype = c_int
         _lib = lib
     return _lib
 
@@ -182,6 +184,12 @@ def gdn_block_set_spin_limit(handle, polls: int) -> None:
 
 def gdn_mxfp6_round_weights(w: int, rows: int, cols: int, codes: int, scales: int, stream: int) -> None:
     rc = load().gdn_mxfp6_round_weights(w, rows, cols, codes, scales, stream)
+    if rc != GDN_OK:
+        raise GdnError(rc, gdn_block_last_error(None))
+
+
+def gdn_read_stream(src: int, nbytes: int, sink: int, stream: int) -> None:
+    rc = load().gdn_read_stream(src, nbytes, sink, stream)
     if rc != GDN_OK:
         raise GdnError(rc, gdn_block_last_error(None))
 

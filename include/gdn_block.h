@@ -270,6 +270,18 @@ int gdn_mxfp4_quantize(const void* x, int32_t rows, int32_t cols, void* codes, v
  * allocates nothing. Errors are reported like gdn_mxfp4_quantize's. */
 int gdn_mxfp6_round_weights(const void* w, int32_t rows, int32_t cols, void* codes, void* scales, void* stream);
 
+/* A plain read of `bytes` bytes of device memory at `src`, the reference that the
+ * block's achieved bandwidth is compared with (a measurement aid, not a step of the
+ * block; the pages measure their kernels against the HBM bandwidth, "vLLM PR #60833",
+ * Validation). Every 16-byte word is read once, with 16-byte loads, 8 in flight per
+ * thread; workgroup b reads the 32 KiB from byte 32768 b on and folds its 32-bit words by
+ * XOR into sink[b], for b < ceil(bytes / 32768) (sink: device, 4-byte aligned,
+ * caller-owned), so the XOR of the sink words equals the XOR of all 32-bit words of the
+ * input. bytes must be a positive
+ * multiple of 16 and src 16-byte aligned. Asynchronous on `stream`; allocates nothing.
+ * Errors are reported like gdn_mxfp4_quantize's. */
+int gdn_read_stream(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Read and clear the handle's sticky error word (synchronous: waits for the whole
  * device first; not for the hot path). Inside a decode, every wait for another
  * workgroup is bounded (gdn_block_set_spin_limit); a wait that gives up sets a bit
@@ -296,8 +308,8 @@ int gdn_block_set_spin_limit(gdn_block_t blk, int32_t polls);
 void gdn_block_destroy(gdn_block_t blk);
 
 /* The last error message of a handle, or of this thread's last failed
- * gdn_block_create, gdn_mxfp4_quantize or gdn_mxfp6_round_weights when blk is NULL. Never NULL; "" when there
- * was none. */
+ * gdn_block_create, gdn_mxfp4_quantize, gdn_mxfp6_round_weights or gdn_read_stream when blk is NULL.
+ * Never NULL; "" when there was none. */
 const char* gdn_block_last_error(gdn_block_t blk);
 
 #ifdef __cplusplus

@@ -137,6 +137,21 @@ def test_quantize_arguments_are_checked_on_the_host():
         assert lib.gdn_mxfp4_quantize(fake, 0, 32, fake, fake, rule, None) == abi.GDN_OK  # nothing to do
 
 
+def test_read_stream_arguments_are_checked_on_the_host():
+    lib = abi.load()
+    fake = 1 << 20  # an aligned address that is never dereferenced: every call below is refused
+    for src, nbytes, sink, needle in [
+        (None, 64, fake, "NULL"),
+        (fake, 64, None, "NULL"),
+        (fake, 0, fake, "multiple of 16"),
+        (fake, 40, fake, "multiple of 16"),
+        (fake + 8, 64, fake, "aligned"),
+        (fake, 64, fake + 2, "aligned"),
+    ]:
+        assert lib.gdn_read_stream(src, nbytes, sink, None) == abi.GDN_E_INVALID_ARG
+        assert needle in abi.gdn_block_last_error(None)
+
+
 def test_null_arguments_are_rejected_on_the_host():
     lib = abi.load()
     assert lib.gdn_block_create(None, None) == abi.GDN_E_INVALID_ARG
