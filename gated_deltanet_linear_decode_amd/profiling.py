@@ -7,6 +7,8 @@
     python -m gated_deltanet_linear_decode_amd.profiling run --raw gpurun_out/prof --verify 1x4,4x4
     python -m gated_deltanet_linear_decode_amd.profiling summarize --raw gpurun_out/prof --verify 1x4,4x4
 
+    python -m gated_deltanet_linear_decode_amd.profiling same-code --rev <git revision> [--restamp]
+
 `run` profiles bench.py (a child process per profile; this process never touches the GPU)
 for each workload in WORKLOADS: a kernel trace with statistics; the HBM byte counters
 FETCH_SIZE and WRITE_SIZE, one pass each; one pass of matrix-core counters; and the
@@ -15,7 +17,11 @@ whose counter readings scale FETCH_SIZE and WRITE_SIZE to bytes. `summarize` tur
 CSV files into one markdown summary per workload and profile, and profiles/hbm_traffic.json
 (bytes per launch, which bench.py reports as roofline.traffic while the kernel source is
 unchanged). With `--verify SxT,...` both take only kernel traces of verify steps (S sequences
-of T tokens on the headline shape) instead.
+of T tokens on the headline shape) instead. `same-code` assembles the kernel source as it
+was at a git revision (which must be the source the summaries were taken from) and as it
+is now, and compares the gfx950 assembly of every kernel the kernel-trace summaries name,
+instruction for instruction (branch-label numbers and comments removed); with `--restamp`,
+when all are the same, it writes the current source hash into the summaries (on the CPU).
 """
 from __future__ import annotations
 
@@ -255,14 +261,73 @@ def summarize_verify(raw: str, profiles: str, steps) -> None:
             f.write("\n".join(lines))
 
 
+def _kernel_asm(src: str, work: str) -> dict:
+    """{demangled kernel name (no parameter list): its gfx950 assembly, branch-label numbers
+    and comments removed} of one source file."""
+    import re
+
+    from gated_deltanet_linear_decode_amd import build
+    out = os.path.join(work, os.path.basename(src) + ".s")
+    flags = [f for f in build.FLAGS if f not in ("-shared", "-fPIC")]
+    subprocess.run([build.HIPCC, *flags, "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), src,
+                    "-o", out], check=True, capture_output=True, text=True)
+    txt = open(out).read()
+    funcs = {m.group(1): m.group(2) for m in re.finditer(r"^(_Z\w+):\s.*?\n(.*?)\n\s*s_endpgm", txt, re.S | re.M)}
+    import shutil
+    filt = shutil.which("c++filt") or shutil.which("llvm-cxxfilt")
+    names = subprocess.run([filt], input="\n".join(funcs), capture_output=True, text=True, check=True).stdout.split("\n")
+    norm = lambda body: "\n".join(ln.split(";")[0].rstrip() for ln in re.sub(r"BB\d+_", "BB_", body).split("\n"))  # noqa: E731
+    return {_short(n): norm(b) for n, b in zip(names, funcs.values())}
+
+
+def same_code(rev: str, profiles: str, restamp: bool) -> bool:
+    import glob
+    import re
+    import tempfile
+    with open(os.path.join(profiles, "hbm_traffic.json")) as f:
+        recorded = json.load(f)["kernel_source_hash"]
+    rel = os.path.relpath(KERNEL_SOURCE, ROOT)
+    with tempfile.TemporaryDirectory() as work:
+        old = os.path.join(work, "old", os.path.basename(KERNEL_SOURCE))
+        os.makedirs(os.path.dirname(old))
+        with open(old, "wb") as f:
+            f.write(subprocess.run(["git", "show", f"{rev}:{rel}"], cwd=ROOT, check=True, capture_output=True).stdout)
+        with open(old, "rb") as f:
+            old_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+        if old_hash != recorded:
+            print(f"[same-code] {rev}:{rel} has hash {old_hash}, the summaries {recorded}: not their source")
+            return False
+        a, b = _kernel_asm(old, work), _kernel_asm(KERNEL_SOURCE, work)
+    names = set()
+    for path in glob.glob(os.path.join(profiles, "*_kernel_trace.md")):
+        names |= set(re.findall(r"^\| `((?:decode|read_stream)_kernel[^`]*)` \|", open(path).read(), re.M))
+    diff = sorted(n for n in names if n not in a or a[n] != b.get(n))
+    for n in sorted(names):
+        print(f"[same-code] {'different' if n in diff else 'same     '} {n}")
+    if diff or not restamp:
+        return not diff
+    new = kernel_source_hash()
+    for path in glob.glob(os.path.join(profiles, "*")):
+        text = open(path).read()
+        if recorded in text:
+            with open(path, "w") as f:
+                f.write(text.replace(recorded, new))
+    print(f"[same-code] summaries stamped {new}")
+    return True
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("action", choices=["run", "summarize"])
+    ap.add_argument("action", choices=["run", "summarize", "same-code"])
     ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof"))
     ap.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--only", default="", help="comma-separated workload:rows pairs (default: every workload)")
     ap.add_argument("--verify", default="", help="comma-separated verify steps SxT: kernel traces of these only")
+    ap.add_argument("--rev", default="HEAD", help="same-code: the git revision the summaries were taken from")
+    ap.add_argument("--restamp", action="store_true", help="same-code: stamp the current hash when all are the same")
     a = ap.parse_args()
+    if a.action == "same-code":
+        raise SystemExit(0 if same_code(a.rev, os.path.abspath(a.profiles), a.restamp) else 1)
     wl = [(w.split(":")[0], int(w.split(":")[1])) for w in a.only.split(",") if w] or None
     ver = [tuple(int(v) for v in p.split("x")) for p in a.verify.split(",") if p]
     if a.action == "run":
