@@ -108,9 +108,17 @@ def test_tiny_verify(R, T, state):
     verify_case(TINY_V.with_(ssm_state_dtype=state), R, T, 600 + 10 * R + T)
 
 
-@pytest.mark.parametrize("R,T", [(4, 4), (2, 3), (8, 2), (5, 3)])
+@pytest.mark.parametrize("R,T", [(4, 4), (2, 3), (8, 2), (5, 3), (1, 16), (2, 7), (16, 1)])
 def test_tp8_rank_verify(R, T):
+    """Up to the most tokens a step takes (16) and an odd count in the chunked form, and 16
+    one-token sequences (the single-token verify launch at its largest)."""
     verify_case(configs.TP8_RANK_BF16, R, T, 700 + 10 * R + T)
+
+
+def test_dense_verify():
+    """The full-width layer: three value heads per key head (two of them hand the key head's
+    old q|k conv rows over to the third) and a K range of 1024 over H = 5120."""
+    verify_case(configs.DENSE_FULL, 2, 4, 731)
 
 
 def test_tp8_rank_f32_residual_verify():
