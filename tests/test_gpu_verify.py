@@ -121,12 +121,19 @@ def test_dense_verify():
     verify_case(configs.DENSE_FULL, 2, 4, 731)
 
 
-def test_tp8_rank_f32_residual_verify():
-    verify_case(configs.TP8_RANK_F32, 5, 3, 711)
+@pytest.mark.parametrize("R,T", [(5, 3), (1, 16)])
+def test_tp8_rank_f32_residual_verify(R, T):
+    verify_case(configs.TP8_RANK_F32, R, T, 711 + 10 * R + T)
 
 
-def test_tp8_rank_mxfp4_verify():
-    verify_case(configs.TP8_RANK_MXFP4, 4, 2, 712, flips=(0.02, 0.15))
+@pytest.mark.parametrize("R,T", [(4, 2), (1, 16)])
+def test_tp8_rank_mxfp4_verify(R, T):
+    verify_case(configs.TP8_RANK_MXFP4, R, T, 712 + 10 * R + T, flips=(0.02, 0.15))
+
+
+def test_tp8_rank_mxfp6_verify():
+    """MXFP6 weights with a residual input (the rstd hand-off)."""
+    verify_case(configs.TP8_RANK_MXFP6, 2, 4, 714)
 
 
 @pytest.mark.parametrize("R,T", [(1, 2), (3, 4)])
