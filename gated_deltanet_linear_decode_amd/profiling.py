@@ -170,8 +170,14 @@ def summarize(raw: str, profiles: str, workloads=None) -> None:
                          f"{r['MaxNs']} | {float(r['Percentage']):.2f} % |")
         gbs = algo / (dec * 1e-9) / 1e9
         lines += ["", f"decode_kernel: {dec / 1000:.2f} µs on average per launch; algorithmic bytes per launch "
-                      f"{algo:,} ({valid} valid rows), so {gbs:.0f} GB/s = {gbs / HBM_PEAK_GBS:.3f} of 8 TB/s.",
-                  "The other kernels are set-up work (weight copies and the tiled-weight pack) outside the timed "
+                      f"{algo:,} ({valid} valid rows), so {gbs:.0f} GB/s = {gbs / HBM_PEAK_GBS:.3f} of 8 TB/s."]
+        rs = [float(r["AverageNs"]) for r in st if _short(r["Name"]) == "read_stream_kernel"]
+        if rs:
+            sgbs = ((algo + 15) // 16 * 16) / (rs[0] * 1e-9) / 1e9
+            lines.append(f"read_stream_kernel: the plain read of the same bytes that bench.py times beside the "
+                         f"block, {rs[0] / 1000:.2f} µs ({sgbs:.0f} GB/s = {sgbs / HBM_PEAK_GBS:.3f} of 8 TB/s); the "
+                         f"block runs at {gbs / sgbs:.3f} of it.")
+        lines += ["The other kernels are set-up work (weight copies and the tiled-weight pack) outside the timed "
                   "graphs.", foot]
         with open(os.path.join(profiles, f"decode_kernel_{t}_kernel_trace.md"), "w") as f:
             f.write("\n".join(lines))
@@ -255,7 +261,8 @@ def summarize_verify(raw: str, profiles: str, steps) -> None:
                          f"{r['MaxNs']} | {float(r['Percentage']):.2f} % |")
         lines += ["", f"The verify launch (`{_short(ver[0]['Name'])}`): {us:.2f} µs on average; algorithmic bytes "
                       f"per launch {algo:,}, so {gbs:.0f} GB/s = {gbs / HBM_PEAK_GBS:.3f} of 8 TB/s. The decode "
-                      "launches with MULTI and DST unset are the short headline run before the verify sweep; the "
+                      "launches with MULTI and DST unset are the short headline run before the verify sweep, and "
+                      "read_stream_kernel the plain read of the headline's bytes that bench.py times beside it; the "
                       "other kernels are set-up work outside the timed graphs.", foot]
         with open(os.path.join(profiles, f"decode_kernel_verify_{seqs}x{tokens}_kernel_trace.md"), "w") as f:
             f.write("\n".join(lines))
